@@ -1,0 +1,263 @@
+// Host planner (see plan.h).
+#include "plan.h"
+
+#include <algorithm>
+#include <array>
+#include <cmath>
+#include <cstdio>
+#include <numeric>
+
+namespace pod {
+
+namespace {
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+pod_status_t fail(std::string* err, pod_status_t st, const char* fmt, long long a = 0,
+                  long long b = 0) {
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), fmt, a, b);
+  if (err) *err = buf;
+  return st;
+}
+
+// MI355X datasheet peaks used only to estimate the prefill share.
+constexpr double kPeakFlops = 2.5e15;   // dense bf16 MFMA, FLOP/s
+constexpr double kPeakBytes = 8.0e12;   // HBM3E, B/s
+constexpr double kPrefillEff = 0.35;    // expected fraction of MFMA peak
+constexpr double kDecodeEff = 0.75;     // expected fraction of HBM peak
+
+}  // namespace
+
+pod_status_t validate(const pod_attn_params_t* p, int32_t np, const int32_t* qo,
+                      const int32_t* pkv, int32_t nd, const int32_t* dkv,
+                      const pod_attn_tuning_t* t, std::string* err) {
+  if (!p) return fail(err, POD_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (p->num_qo_heads < 1 || p->num_kv_heads < 1)
+    return fail(err, POD_ERR_INVALID_ARGUMENT, "head counts must be >= 1 (got %lld, %lld)",
+                p->num_qo_heads, p->num_kv_heads);
+  if (p->num_qo_heads % p->num_kv_heads != 0)
+    return fail(err, POD_ERR_INVALID_ARGUMENT,
+                "num_qo_heads (%lld) is not a multiple of num_kv_heads (%lld)",
+                p->num_qo_heads, p->num_kv_heads);
+  if (p->head_dim != kHeadDim)
+    return fail(err, POD_ERR_UNSUPPORTED, "head_dim %lld unsupported (only 128)", p->head_dim);
+  if (p->kv_layout != POD_KV_CONTIGUOUS && p->kv_layout != POD_KV_PAGED)
+    return fail(err, POD_ERR_INVALID_ARGUMENT, "kv_layout %lld invalid", p->kv_layout);
+  if (p->kv_layout == POD_KV_PAGED && (!is_pow2(p->page_size) || p->page_size > 1024))
+    return fail(err, POD_ERR_INVALID_ARGUMENT,
+                "page_size %lld must be a power of two in [1, 1024]", p->page_size);
+  if (p->causal != 0 && p->causal != 1)
+    return fail(err, POD_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %lld)", p->causal);
+  if (!(std::isfinite(p->sm_scale) && p->sm_scale > 0.0f))
+    return fail(err, POD_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
+  if (np < 0 || nd < 0)
+    return fail(err, POD_ERR_INVALID_ARGUMENT, "negative request count (%lld, %lld)", np, nd);
+  if (np > 0 && (!qo || !pkv))
+    return fail(err, POD_ERR_INVALID_ARGUMENT, "prefill length arrays are NULL");
+  if (nd > 0 && !dkv)
+    return fail(err, POD_ERR_INVALID_ARGUMENT, "decode length array is NULL");
+  const int64_t kMaxLen = int64_t(1) << 24;
+  int64_t sum_qo = 0;
+  for (int32_t i = 0; i < np; ++i) {
+    if (qo[i] < 1) return fail(err, POD_ERR_INVALID_ARGUMENT,
+                               "prefill %lld: qo_len %lld < 1", i, qo[i]);
+    if (pkv[i] < qo[i]) return fail(err, POD_ERR_INVALID_ARGUMENT,
+                                    "prefill %lld: kv_len < qo_len (kv %lld)", i, pkv[i]);
+    if (pkv[i] > kMaxLen) return fail(err, POD_ERR_UNSUPPORTED,
+                                      "prefill %lld: kv_len %lld too large", i, pkv[i]);
+    sum_qo += qo[i];
+  }
+  for (int32_t i = 0; i < nd; ++i) {
+    if (dkv[i] < 1) return fail(err, POD_ERR_INVALID_ARGUMENT,
+                                "decode %lld: kv_len %lld < 1", i, dkv[i]);
+    if (dkv[i] > kMaxLen) return fail(err, POD_ERR_UNSUPPORTED,
+                                      "decode %lld: kv_len %lld too large", i, dkv[i]);
+  }
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  if (sum_qo * p->num_qo_heads > lim || int64_t(nd) * p->num_qo_heads > lim)
+    return fail(err, POD_ERR_UNSUPPORTED, "too many (row, head) outputs");
+  if (t) {
+    if (t->wgs_per_cu != 0 && t->wgs_per_cu != 2)
+      return fail(err, POD_ERR_UNSUPPORTED, "wgs_per_cu %lld unsupported (0 or 2)",
+                  t->wgs_per_cu);
+    if (t->prefill_quarters_per_cu < -1 || t->prefill_quarters_per_cu > 8)
+      return fail(err, POD_ERR_INVALID_ARGUMENT, "prefill_quarters_per_cu %lld out of [-1, 8]",
+                  t->prefill_quarters_per_cu);
+    if (t->prefill_kv_splits < 0 || t->decode_kv_splits < 0)
+      return fail(err, POD_ERR_INVALID_ARGUMENT, "negative forced split count");
+    if (t->sched_mode < 0 || t->sched_mode > POD_SCHED_ORDERED)
+      return fail(err, POD_ERR_INVALID_ARGUMENT, "sched_mode %lld invalid", t->sched_mode);
+    if (t->match_sequential != 0 && t->match_sequential != 1)
+      return fail(err, POD_ERR_INVALID_ARGUMENT, "match_sequential must be 0 or 1");
+  }
+  return POD_OK;
+}
+
+int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu) {
+  const auto& p = b.params;
+  const int32_t full = 4 * wgs_per_cu;
+  if (b.qo.empty()) return 0;
+  if (b.dkv.empty()) return full;
+  double pairs_p = 0.0, keys_d = 0.0;
+  for (size_t i = 0; i < b.qo.size(); ++i) {
+    double q = b.qo[i], k = b.pkv[i];
+    pairs_p += p.causal ? q * (k - q) + q * (q + 1) / 2 : q * k;
+  }
+  for (int32_t k : b.dkv) keys_d += k;
+  const double f = 4.0 * kHeadDim * p.num_qo_heads * pairs_p;
+  const double by = keys_d * p.num_kv_heads * kHeadDim * 2.0 * 2.0;
+  const double tp = f / (kPeakFlops * kPrefillEff);
+  const double td = by / (kPeakBytes * kDecodeEff);
+  int32_t q = (int32_t)std::lround(full * tp / (tp + td));
+  return std::min(full - 1, std::max(1, q));
+}
+
+void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_slots,
+                 int64_t decode_wave_slots, int32_t force_p_splits, int32_t force_d_splits,
+                 WorkLists* out) {
+  const auto& p = b.params;
+  const int32_t hq = p.num_qo_heads, hkv = p.num_kv_heads, g = hq / hkv;
+  const int32_t np = (int32_t)b.qo.size(), nd = (int32_t)b.dkv.size();
+  WorkLists w;
+  int32_t n_partials = 0;
+
+  // ---- prefill tiles (request, query head, 128-row block) ----
+  struct Tile { int32_t qrow0, head, nrows, pos0, kv_end, req, kvh; };
+  std::vector<Tile> tiles;
+  int32_t qrow = 0;
+  for (int32_t r = 0; r < np; ++r) {
+    const int32_t qo = b.qo[r], kv = b.pkv[r];
+    for (int32_t h = 0; h < hq; ++h)
+      for (int32_t r0 = 0; r0 < qo; r0 += kPrefillRows) {
+        Tile t;
+        t.qrow0 = qrow + r0;
+        t.head = h;
+        t.nrows = std::min(kPrefillRows, qo - r0);
+        t.pos0 = kv - qo + r0;
+        t.kv_end = p.causal ? std::min(kv, t.pos0 + t.nrows) : kv;
+        t.req = r;
+        t.kvh = h / g;
+        tiles.push_back(t);
+      }
+    qrow += qo;
+  }
+  // order: KV head major, so that one XCD pool holds the tiles sharing K/V
+  std::stable_sort(tiles.begin(), tiles.end(), [](const Tile& a, const Tile& c) {
+    return a.kvh < c.kvh;
+  });
+  int32_t s_all = 1;
+  if (force_p_splits > 0) {
+    s_all = force_p_splits;
+  } else if (!tiles.empty()) {
+    // [POD] "Cap prefill splitting": at most two waves of the slots.
+    s_all = (int32_t)std::max<int64_t>(1, (2 * prefill_slots) / (int64_t)tiles.size());
+    s_all = std::min(s_all, kMaxPrefillSplits);
+  }
+  struct PI { std::vector<int32_t> f; double work; };
+  std::vector<PI> pitems;
+  for (const Tile& t : tiles) {
+    const int32_t n_kt = (int32_t)ceil_div(t.kv_end, kPrefillKeys);
+    int32_t s = std::max(1, std::min(s_all, n_kt));
+    const int32_t per = (int32_t)ceil_div(n_kt, s);
+    s = (int32_t)ceil_div(n_kt, per);
+    int32_t base = -1;
+    if (s > 1) {
+      base = n_partials;
+      n_partials += s * kPrefillRows;
+      for (int32_t i = 0; i < t.nrows; ++i) {
+        w.m_tasks.push_back((t.qrow0 + i) * hq + t.head);
+        w.m_tasks.push_back(base + i);
+        w.m_tasks.push_back(kPrefillRows);
+        w.m_tasks.push_back(s);
+      }
+    }
+    w.p_splits_max = std::max(w.p_splits_max, s);
+    for (int32_t k = 0; k < s; ++k) {
+      const int32_t kb = k * per * kPrefillKeys;
+      const int32_t ke = std::min(t.kv_end, (k + 1) * per * kPrefillKeys);
+      PI it;
+      it.f = {t.qrow0, t.head, t.nrows, t.pos0, kb, ke, t.req,
+              base < 0 ? -1 : base + k * kPrefillRows};
+      it.work = double(t.nrows) * double(ke - kb);
+      pitems.push_back(std::move(it));
+    }
+  }
+  // ---- XCD pools: contiguous runs of the KV-head-ordered list, equal work ----
+  const int32_t nx = std::max(1, std::min(dev.num_xcds, kMaxXcds));
+  double total = 0.0;
+  for (auto& it : pitems) total += it.work;
+  w.pool_off.assign(nx + 1, 0);
+  {
+    double acc = 0.0;
+    int32_t x = 0;
+    for (size_t i = 0; i < pitems.size(); ++i) {
+      // item i goes to pool x where x = floor(acc_mid / share)
+      const double mid = acc + 0.5 * pitems[i].work;
+      int32_t want = total > 0 ? (int32_t)std::floor(mid * nx / total) : 0;
+      want = std::min(nx - 1, std::max(x, want));
+      while (x < want) w.pool_off[++x] = (int32_t)i;
+      acc += pitems[i].work;
+    }
+    while (x < nx) w.pool_off[++x] = (int32_t)pitems.size();
+  }
+  for (auto& it : pitems) w.p_items.insert(w.p_items.end(), it.f.begin(), it.f.end());
+
+  // ---- decode units (request, KV head, <=16 query heads, split) ----
+  const int32_t qchunks = (int32_t)ceil_div(g, kDecodeRows);
+  double total_keys = 0.0;
+  for (int32_t k : b.dkv) total_keys += double(k) * hkv * qchunks;
+  int64_t chunk = kMinDecodeChunk;
+  if (decode_wave_slots > 0 && total_keys > 0) {
+    const int64_t c = (int64_t)std::ceil(total_keys / double(2 * decode_wave_slots));
+    chunk = std::max<int64_t>(chunk, ceil_div(c, kDecodeStep) * kDecodeStep);
+  }
+  struct DI { std::array<int32_t, D_FIELDS> f; int32_t work; };
+  std::vector<DI> ditems;
+  for (int32_t i = 0; i < nd; ++i) {
+    const int32_t kv = b.dkv[i];
+    const int32_t steps = (int32_t)ceil_div(kv, kDecodeStep);
+    int64_t s64 = force_d_splits > 0
+                      ? force_d_splits
+                      : std::min<int64_t>(ceil_div(kv, chunk), kMaxDecodeSplits);
+    int32_t s = (int32_t)std::max<int64_t>(1, std::min<int64_t>(s64, steps));
+    const int32_t per = (int32_t)ceil_div(steps, s);
+    s = (int32_t)ceil_div(steps, per);
+    int32_t region = -1;
+    if (s > 1) {
+      region = n_partials;
+      n_partials += hq * s;
+      for (int32_t h = 0; h < hq; ++h) {
+        w.m_tasks.push_back(i * hq + h);
+        w.m_tasks.push_back(region + h * s);
+        w.m_tasks.push_back(1);
+        w.m_tasks.push_back(s | (1 << 16));
+      }
+    }
+    w.d_splits_max = std::max(w.d_splits_max, s);
+    for (int32_t kh = 0; kh < hkv; ++kh)
+      for (int32_t qc = 0; qc < qchunks; ++qc) {
+        const int32_t h0 = kh * g + qc * kDecodeRows;
+        const int32_t nq = std::min(kDecodeRows, g - qc * kDecodeRows);
+        for (int32_t k = 0; k < s; ++k) {
+          const int32_t kb = k * per * kDecodeStep;
+          const int32_t ke = std::min(kv, (k + 1) * per * kDecodeStep);
+          DI it;
+          it.f = {i, h0, nq, kb, ke, np + i, region < 0 ? -1 : region + h0 * s + k,
+                  region < 0 ? 0 : s};
+          it.work = ke - kb;
+          ditems.push_back(it);
+        }
+      }
+  }
+  // longest first, so that the four waves of a decode workgroup get similar work
+  std::stable_sort(ditems.begin(), ditems.end(),
+                   [](const DI& a, const DI& c) { return a.work > c.work; });
+  for (auto& it : ditems) w.d_items.insert(w.d_items.end(), it.f.begin(), it.f.end());
+  w.n_partials = n_partials;
+  *out = std::move(w);
+}
+
+}  // namespace pod

@@ -1,0 +1,107 @@
+// Host planner for one hybrid batch: work lists, KV splits, prefill:decode
+// mix.  Pure C++ (no HIP), so it can be tested and sanitised on a CPU.
+//
+// Sources: [POD] "POD-Attention: Unlocking Full Prefill-Decode Overlap for
+// Faster LLM Inference", section "How POD-Attention overlaps" (remapped
+// work identities, per-SM role tickets, 2 or 4 blocks per SM, KV splits
+// capped at two waves) and "The idea" (proportional, not 50:50, allocation);
+// [PR] "Limit kv split when prefill tokens <= 1536" (split count of small
+// prefills accounts for co-located decode workgroups).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/pod_attn.h"
+
+namespace pod {
+
+// Tile shapes shared by planner and kernels.
+constexpr int kHeadDim = 128;
+constexpr int kPrefillRows = 128;   // query rows per prefill workgroup (4 waves x 32)
+constexpr int kPrefillKeys = 64;    // keys per prefill KV tile
+constexpr int kDecodeStep = 32;     // keys per decode step (2 MFMA key blocks)
+constexpr int kDecodeRows = 16;     // decode query tile (MFMA 16 rows)
+constexpr int kWavesPerWG = 4;
+constexpr int kMaxXcds = 16;
+constexpr int kMaxPrefillSplits = 16;
+constexpr int kMaxDecodeSplits = 64;
+constexpr int kMinDecodeChunk = 512;   // keys per decode split, lower bound
+
+// Prefill work item (8 int32).
+enum PItem : int {
+  P_QROW0 = 0,    // global row of q_prefill holding the tile's first row
+  P_HEAD = 1,     // query head
+  P_NROWS = 2,    // valid rows, 1..kPrefillRows
+  P_POS0 = 3,     // absolute position of the first row (kv_len - qo_len + row)
+  P_KV_BEGIN = 4, // first key of this split (multiple of kPrefillKeys)
+  P_KV_END = 5,   // one past the last key this split may read
+  P_KVREQ = 6,    // request index into kv_indptr / page_indptr
+  P_PART = 7,     // -1: write O/LSE; else partial index of row 0 (row i: +i)
+  P_FIELDS = 8
+};
+
+// Decode work item (8 int32): one wavefront's unit.
+enum DItem : int {
+  D_QROW = 0,     // decode request index (row of q_decode)
+  D_HEAD0 = 1,    // first query head of the unit (all share one KV head)
+  D_NQ = 2,       // query heads, 1..kDecodeRows
+  D_KV_BEGIN = 3, // first key (multiple of kDecodeStep)
+  D_KV_END = 4,   // one past the last key
+  D_KVREQ = 5,    // request index into kv_indptr / page_indptr
+  D_PART = 6,     // -1: write O/LSE; else partial index of head D_HEAD0
+  D_PSTRIDE = 7,  // partial index step between consecutive heads
+  D_FIELDS = 8
+};
+
+// Merge task (4 int32): one (row, head) combined from n partials.
+enum MTask : int {
+  M_OUT = 0,      // row * Hq + head in o_prefill/o_decode (elements of 128)
+  M_BASE = 1,     // partial index of split 0
+  M_STRIDE = 2,   // partial index step between splits
+  M_NFLAG = 3,    // n_splits | (is_decode << 16)
+  M_FIELDS = 4
+};
+
+struct WorkLists {
+  std::vector<int32_t> p_items;    // P_FIELDS each, grouped by XCD pool
+  std::vector<int32_t> pool_off;   // num_xcds + 1 offsets (items) into p_items
+  std::vector<int32_t> d_items;    // D_FIELDS each, in groups of kWavesPerWG
+  std::vector<int32_t> m_tasks;    // M_FIELDS each
+  int32_t n_partials = 0;
+  int32_t p_splits_max = 1;
+  int32_t d_splits_max = 1;
+  int32_t n_p() const { return (int32_t)(p_items.size() / P_FIELDS); }
+  int32_t n_d() const { return (int32_t)(d_items.size() / D_FIELDS); }
+  int32_t n_groups() const { return (n_d() + kWavesPerWG - 1) / kWavesPerWG; }
+  int32_t n_m() const { return (int32_t)(m_tasks.size() / M_FIELDS); }
+};
+
+struct Batch {
+  pod_attn_params_t params;
+  std::vector<int32_t> qo, pkv, dkv;   // prefill qo/kv, decode kv
+};
+
+struct PlanChoice {
+  int32_t wgs_per_cu = 2;
+  int32_t prefill_quarters = 4;        // target prefill WGs per CU, in quarters
+  int32_t sched_mode = POD_SCHED_LIVE;
+};
+
+// Validation of parameters and lengths; returns POD_OK or an error with text.
+pod_status_t validate(const pod_attn_params_t* p, int32_t np, const int32_t* qo,
+                      const int32_t* pkv, int32_t nd, const int32_t* dkv,
+                      const pod_attn_tuning_t* t, std::string* err);
+
+// Proportional prefill share ([POD] "The idea"): quarters of a CU's
+// workgroup slots given to prefill, from estimated prefill/decode times.
+int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu);
+
+// Builds one set of work lists.  `prefill_slots` / `decode_wave_slots` are the
+// concurrent prefill workgroups / decode wavefronts the splits should fill.
+void build_lists(const Batch& b, const pod_device_desc_t& dev,
+                 int64_t prefill_slots, int64_t decode_wave_slots,
+                 int32_t force_p_splits, int32_t force_d_splits, WorkLists* out);
+
+}  // namespace pod

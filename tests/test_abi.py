@@ -1,0 +1,137 @@
+"""C ABI: the library loads without a GPU, exports every declared symbol, and
+rejects invalid arguments with status codes (no compute calls here)."""
+
+import ctypes as C
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from prefill_decode_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    src = open(os.path.join(ROOT, "include", "pod_attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pod_attn_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    declared = _declared_symbols()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(B.EXPORTED)
+
+
+def _plan_status(params, qo, kv, dkv, tuning=None):
+    lib = B.lib()
+    qo, kv, dkv = (np.ascontiguousarray(np.asarray(x, np.int32)) for x in (qo, kv, dkv))
+    h = C.c_void_p(0)
+    dev = B.DeviceDesc(256, 8)
+    st = lib.pod_attn_plan_host(C.byref(params), len(qo), B._ptr(qo), B._ptr(kv), len(dkv),
+                                B._ptr(dkv), C.byref(tuning) if tuning else None,
+                                C.byref(dev), C.byref(h))
+    if h.value:
+        lib.pod_attn_plan_destroy(h)
+    return st
+
+
+OK, INV, UNS = 0, 1, 2
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(qo=[5], kv=[4], dkv=[]), INV),                    # qo > kv
+    (dict(qo=[0], kv=[4], dkv=[]), INV),                    # qo = 0
+    (dict(qo=[], kv=[], dkv=[0]), INV),                     # decode kv = 0
+    (dict(qo=[], kv=[], dkv=[-3]), INV),
+    (dict(qo=[4], kv=[4], dkv=[7]), OK),
+    (dict(qo=[], kv=[], dkv=[]), OK),                       # empty batch is valid
+    (dict(hq=6, hkv=4), INV),                               # Hq % Hkv != 0
+    (dict(hq=0, hkv=1), INV),
+    (dict(head_dim=64), UNS),
+    (dict(page_size=12), INV),
+    (dict(page_size=0), INV),
+    (dict(page_size=2048), INV),
+    (dict(page_size=1), OK),
+    (dict(page_size=8), OK),
+    (dict(sm_scale=0.0), INV),
+    (dict(sm_scale=-1.0), INV),
+    (dict(sm_scale=float("nan")), INV),
+    (dict(sm_scale=float("inf")), INV),
+    (dict(layout=7), INV),
+    (dict(causal=2), INV),
+    (dict(qo=[3], kv=[1 << 25], dkv=[]), UNS),
+])
+def test_plan_validation(case, expect):
+    p = B.make_params(case.get("hq", 8), case.get("hkv", 2), "paged",
+                      case.get("page_size", 16), True,
+                      case.get("sm_scale", 1 / math.sqrt(128)), case.get("head_dim", 128))
+    if "layout" in case:
+        p.kv_layout = case["layout"]
+    if "causal" in case:
+        p.causal = case["causal"]
+    st = _plan_status(p, case.get("qo", [4]), case.get("kv", [9]), case.get("dkv", [5]))
+    assert st == expect, (st, B.last_error())
+    if st != OK:
+        assert B.last_error()
+
+
+@pytest.mark.parametrize("tun,expect", [
+    (dict(wgs_per_cu=4), UNS), (dict(wgs_per_cu=3), UNS), (dict(wgs_per_cu=2), OK),
+    (dict(prefill_quarters_per_cu=9), INV), (dict(prefill_quarters_per_cu=-2), INV),
+    (dict(prefill_kv_splits=-1), INV), (dict(decode_kv_splits=-1), INV),
+    (dict(sched_mode=3), INV), (dict(match_sequential=2), INV),
+    (dict(sched_mode=B.SCHED_TICKET, prefill_quarters_per_cu=8), OK),
+])
+def test_tuning_validation(tun, expect):
+    p = B.make_params(8, 2)
+    st = _plan_status(p, [4], [9], [5], B.make_tuning(**tun))
+    assert st == expect, (st, B.last_error())
+
+
+def test_null_length_arrays_rejected():
+    lib = B.lib()
+    p = B.make_params(8, 2)
+    h = C.c_void_p(0)
+    dev = B.DeviceDesc(256, 8)
+    st = lib.pod_attn_plan_host(C.byref(p), 2, None, None, 0, None, None, C.byref(dev),
+                                C.byref(h))
+    assert st == INV and not h.value
+    st = lib.pod_attn_plan_host(C.byref(p), 0, None, None, 3, None, None, C.byref(dev),
+                                C.byref(h))
+    assert st == INV and not h.value
+    st = lib.pod_attn_plan_host(None, 0, None, None, 0, None, None, C.byref(dev), C.byref(h))
+    assert st == INV
+    st = lib.pod_attn_plan_host(C.byref(p), 0, None, None, 0, None, None, None, C.byref(h))
+    assert st == INV
+    bad = B.DeviceDesc(0, 8)
+    st = lib.pod_attn_plan_host(C.byref(p), 0, None, None, 0, None, None, C.byref(bad),
+                                C.byref(h))
+    assert st == INV
+
+
+def test_host_plan_cannot_run_and_null_handles():
+    lib = B.lib()
+    pl = B.plan_host(B.make_params(8, 2), [4], [9], [5])
+    t = B.Tensors()
+    st = lib.pod_attn_run(pl.handle, C.byref(t), None)
+    assert st == INV and "workspace" in B.last_error()
+    st = lib.pod_attn_sequential_run(pl.handle, C.byref(t), None)
+    assert st == INV
+    assert lib.pod_attn_run(None, C.byref(t), None) == INV
+    assert lib.pod_attn_run(pl.handle, None, None) == INV
+    assert lib.pod_attn_plan_info(None, None) == INV
+    cnt = C.c_size_t(0)
+    assert lib.pod_attn_plan_export(pl.handle, 99, None, 0, C.byref(cnt)) == INV
+    assert lib.pod_attn_read_trace(pl.handle, None, 0, C.byref(cnt), None) == INV
+    assert lib.pod_attn_probe_hwid(0, None, None) == INV
+    lib.pod_attn_plan_destroy(None)   # no-op
+    info = pl.info()
+    assert info["workspace_bytes"] > 0 and info["prefill_items"] == 8   # 8 heads x 1 block
+    pl.destroy()

@@ -1,0 +1,78 @@
+"""GPU parity at the full workload sizes (the launch configuration the bench
+times), checked on sampled rows the oracle computes one by one, plus the
+scheduler's co-location trace on the Llama-3-8B-shaped batch."""
+
+import numpy as np
+import pytest
+
+import oracle
+from prefill_decode_amd import binding as B
+from prefill_decode_amd import inputs
+from tests.gpu_util import compare, run_path, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(spec, rng):
+    qo = np.array(spec.prefill_qo_len)
+    offs = np.concatenate([[0], np.cumsum(qo)])
+    rows = set()
+    for r in range(len(qo)):
+        a, b = int(offs[r]), int(offs[r + 1])
+        rows.update([a, min(a + 1, b - 1), b - 1, max(a, b - 2)])
+        rows.update(int(x) for x in rng.integers(a, b, size=min(8, b - a)))
+    dkv = np.array(spec.decode_kv_len)
+    dec = {int(np.argmax(dkv)), int(np.argmin(dkv)), 0, len(dkv) - 1}
+    dec.update(int(x) for x in rng.choice(len(dkv), size=min(8, len(dkv)), replace=False))
+    return sorted(rows), sorted(dec)
+
+
+@pytest.mark.parametrize("name", inputs.CONFIG_NAMES)
+def test_fullsize_sampled(name):
+    import torch
+    spec = inputs.config_spec(name)
+    say(f"[fullsize] {name}: generating on device")
+    bd = inputs.make_batch_device(spec, poison=True)
+    runner = B.BatchRunner(bd)
+    rows, dec = _sample(spec, np.random.default_rng(5))
+    sub = inputs.host_subset(bd, list(range(spec.num_prefill)), dec)
+    say(f"  oracle on {len(rows)} prefill rows, {len(dec)} decodes")
+    ref = oracle.sample_batch_attention(sub, rows, list(range(len(dec))))
+    for path in ("fused", "seq"):
+        say(f"  path {path}")
+        got = run_path(runner, path)
+        g = {"o_prefill": got["o_prefill"][rows], "lse_prefill": got["lse_prefill"][rows],
+             "o_decode": got["o_decode"][dec], "lse_decode": got["lse_decode"][dec]}
+        compare(g, ref, f"{name}/{path}")
+        # every output row written and finite (full check of the non-sampled rows)
+        for k in got:
+            assert np.all(np.isfinite(got[k])), (name, path, k)
+    del runner, bd
+    torch.cuda.empty_cache()
+
+
+def test_colocation_trace():
+    spec = inputs.config_spec("llama3_8b")
+    say("[trace] llama3_8b")
+    bd = inputs.make_batch_device(spec)
+    runner = B.BatchRunner(bd, B.make_tuning(flags=B.FLAG_TRACE))
+    run_path(runner, "fused")
+    info = runner.plan.info()
+    tr = runner.plan.read_trace()
+    assert len(tr) == info["prefill_items"] + info["decode_groups"]
+    role, unit, slot = tr[:, 2], tr[:, 3], tr[:, 1]
+    assert sorted(unit[role == 0].tolist()) == list(range(info["prefill_items"]))
+    assert sorted(unit[role == 1].tolist()) == list(range(info["decode_groups"]))
+    both = 0
+    slots = np.unique(slot)
+    for s in slots:
+        m = slot == s
+        p = tr[m & (role == 0)]
+        d = tr[m & (role == 1)]
+        if len(p) and len(d):
+            ov = (np.minimum(p[:, 5][:, None], d[:, 5][None, :]) >
+                  np.maximum(p[:, 4][:, None], d[:, 4][None, :]))
+            both += int(ov.any())
+    say(f"  CUs used {len(slots)}, CUs running prefill and decode at once {both}")
+    assert len(slots) == 256
+    assert both >= 0.5 * len(slots)

@@ -1,0 +1,223 @@
+"""Host planner invariants (CPU, through pod_attn_plan_host).
+
+Every (row, head) is covered by exactly one prefill tile or decode unit group,
+whose KV splits partition the visible keys; partial slots are disjoint and the
+merge tasks reference exactly them; XCD pools partition the prefill list; the
+split caps and the proportional mix follow the planner's rules."""
+
+import numpy as np
+import pytest
+
+from prefill_decode_amd import binding as B
+from prefill_decode_amd import inputs
+
+# item layouts (include/pod_attn.h, pod_attn_plan_export)
+P_F, D_F, M_F = 8, 8, 4
+
+
+def _spec_lists(spec, **tun):
+    p = B.make_params(spec.num_qo_heads, spec.num_kv_heads, spec.layout, spec.page_size,
+                      spec.causal, spec.sm_scale)
+    t = B.make_tuning(**tun) if tun else None
+    pl = B.plan_host(p, spec.prefill_qo_len, spec.prefill_kv_len, spec.decode_kv_len, t)
+    return pl
+
+
+def _check_lists(spec, pitems, ditems, mtasks, pool_off, n_partials):
+    hq, hkv = spec.num_qo_heads, spec.num_kv_heads
+    g = hq // hkv
+    qo = np.array(spec.prefill_qo_len, dtype=np.int64)
+    kv = np.array(spec.prefill_kv_len, dtype=np.int64)
+    offs = np.concatenate([[0], np.cumsum(qo)])
+    P = pitems.reshape(-1, P_F)
+    D = ditems.reshape(-1, D_F)
+    M = mtasks.reshape(-1, M_F)
+    used = np.zeros(max(n_partials, 1), dtype=np.int32)
+
+    # ---- prefill: group items by tile (qrow0, head) ----
+    tiles = {}
+    for it in P:
+        tiles.setdefault((int(it[0]), int(it[1])), []).append(it)
+    covered = np.zeros((int(offs[-1]), hq), dtype=np.int32)
+    split_of_row = {}
+    for (qrow0, h), its in tiles.items():
+        its = sorted(its, key=lambda x: x[4])
+        r = int(its[0][6])
+        nrows, pos0 = int(its[0][2]), int(its[0][3])
+        assert all(int(x[2]) == nrows and int(x[3]) == pos0 and int(x[6]) == r for x in its)
+        assert offs[r] <= qrow0 and qrow0 + nrows <= offs[r + 1]
+        row_in_req = qrow0 - offs[r]
+        assert pos0 == kv[r] - qo[r] + row_in_req            # bottom-right alignment
+        end = min(kv[r], pos0 + nrows) if spec.causal else kv[r]
+        # splits partition [0, end) on 64-key boundaries
+        assert int(its[0][4]) == 0 and int(its[-1][5]) == end
+        for a, b in zip(its[:-1], its[1:]):
+            assert int(a[5]) == int(b[4]) and int(b[4]) % 64 == 0
+        assert all(int(x[4]) < int(x[5]) for x in its)
+        covered[qrow0:qrow0 + nrows, h] += 1
+        parts = [int(x[7]) for x in its]
+        if len(its) == 1:
+            assert parts == [-1]
+        else:
+            assert all(p >= 0 for p in parts)
+            for p in parts:
+                assert np.all(used[p:p + nrows] == 0)
+                used[p:p + nrows] += 1
+            for i in range(nrows):
+                split_of_row[((qrow0 + i) * hq + h, 0)] = (parts[0] + i, parts, len(its))
+    assert np.all(covered == 1)
+
+    # ---- decode: units partition heads x keys ----
+    dkv = np.array(spec.decode_kv_len, dtype=np.int64)
+    n_p = len(qo)
+    per_req = {}
+    for it in D:
+        per_req.setdefault(int(it[0]), []).append(it)
+    assert sorted(per_req) == list(range(len(dkv)))
+    for i, its in per_req.items():
+        heads = {}
+        for it in its:
+            h0, nq = int(it[1]), int(it[2])
+            assert 1 <= nq <= 16 and h0 // g == (h0 + nq - 1) // g    # one KV head
+            assert int(it[5]) == n_p + i
+            heads.setdefault((h0, nq), []).append(it)
+        hcov = np.zeros(hq, dtype=np.int32)
+        nsplit = None
+        for (h0, nq), sp in heads.items():
+            hcov[h0:h0 + nq] += 1
+            sp = sorted(sp, key=lambda x: x[3])
+            assert int(sp[0][3]) == 0 and int(sp[-1][4]) == dkv[i]
+            for a, b in zip(sp[:-1], sp[1:]):
+                assert int(a[4]) == int(b[3]) and int(b[3]) % 32 == 0
+            nsplit = len(sp) if nsplit is None else nsplit
+            assert len(sp) == nsplit
+            for it in sp:
+                if nsplit == 1:
+                    assert int(it[6]) == -1
+                else:
+                    for jj in range(nq):
+                        p = int(it[6]) + jj * int(it[7])
+                        assert used[p] == 0
+                        used[p] += 1
+        assert np.all(hcov == 1)
+    # ---- merge tasks cover exactly the split rows ----
+    seen = set()
+    for t in M:
+        out, base, stride, nf = (int(x) for x in t)
+        n, dec = nf & 0xFFFF, nf >> 16
+        assert n >= 2
+        assert (out, dec) not in seen
+        seen.add((out, dec))
+        for s in range(n):
+            assert used[base + s * stride] == 1
+            used[base + s * stride] = 2
+    assert np.all(used[:n_partials] != 1), "a partial slot is written but never merged"
+    # ---- pools ----
+    po = np.asarray(pool_off)
+    assert po[0] == 0 and po[-1] == len(P) and np.all(np.diff(po) >= 0)
+
+
+def _specs():
+    S = inputs.custom_spec
+    out = [inputs.config_spec(n) for n in inputs.CONFIG_NAMES]
+    out += [inputs.config_spec("batched", n_dec=n) for n in (32, 64, 128, 256)]
+    out += [
+        S("ragged", 12, 4, [(1, 1), (129, 300), (7, 7), (300, 1000)], [1, 31, 33, 500], seed=1),
+        S("gqa32", 64, 2, [(200, 200)], [4000, 17], seed=2),        # 32 q heads per kv head
+        S("only_prefill", 8, 8, [(513, 2000)], [], seed=3),
+        S("only_decode", 32, 8, [], [1, 2, 3, 40000], seed=4),
+        S("noncausal", 4, 2, [(100, 250)], [9], seed=5, causal=False),
+        S("page1", 4, 1, [(5, 70)], [65], seed=6, page_size=1),
+        S("page64", 8, 2, [(70, 140)], [1000], seed=7, page_size=64),
+        S("empty", 4, 2, [], [], seed=8),
+    ]
+    return out
+
+
+@pytest.mark.parametrize("spec", _specs(), ids=lambda s: s.name)
+@pytest.mark.parametrize("tun", [{}, dict(prefill_kv_splits=3, decode_kv_splits=5),
+                                 dict(match_sequential=1), dict(prefill_quarters_per_cu=1)],
+                         ids=["auto", "forced", "matched", "q1"])
+def test_lists_cover_and_partition(spec, tun):
+    pl = _spec_lists(spec, **tun)
+    info = pl.info()
+    for which_p, which_d, which_m, which_pool in ((0, 1, 2, 6), (3, 4, 5, 7)):
+        _check_lists(spec, pl.export(which_p), pl.export(which_d), pl.export(which_m),
+                     pl.export(which_pool), info["num_partials"])
+    if tun.get("match_sequential"):
+        for a, b in ((0, 3), (1, 4), (2, 5)):
+            assert np.array_equal(pl.export(a), pl.export(b))
+
+
+def test_forced_splits_are_honoured():
+    spec = inputs.custom_spec("f", 8, 2, [(128, 4096)], [4096, 100], seed=9)
+    pl = _spec_lists(spec, prefill_kv_splits=4, decode_kv_splits=8)
+    P = pl.export(0).reshape(-1, P_F)
+    D = pl.export(1).reshape(-1, D_F)
+    assert len(P) == 8 * 4                      # 8 heads x 1 block x 4 splits
+    d0 = D[D[:, 0] == 0]
+    assert len(d0) == 2 * 8                     # 2 kv heads x 8 splits
+    d1 = D[D[:, 0] == 1]
+    assert len(d1) == 2 * 4                     # 100 keys: at most ceil(100/32) splits
+
+
+def test_split_cap_two_waves():
+    # [POD] "Cap prefill splitting": tiles x splits <= 2 x slots
+    for spec in _specs():
+        pl = _spec_lists(spec, match_sequential=0)
+        P = pl.export(3).reshape(-1, P_F)
+        tiles = {(int(r[0]), int(r[1])) for r in P}
+        if len(tiles):
+            assert len(P) <= max(len(tiles), 2 * 256 * 2), spec.name
+        D = pl.export(4).reshape(-1, D_F)
+        per = {}
+        for r in D:
+            per.setdefault((int(r[0]), int(r[1])), 0)
+            per[(int(r[0]), int(r[1]))] += 1
+        assert max(per.values(), default=1) <= 64
+
+
+def test_small_prefill_regime_accounts_for_colocated_decode():
+    # [PR] "Limit kv split when prefill tokens <= 1536": the fused plan's
+    # prefill splits fill only the slots beside the co-located decode WGs.
+    spec = inputs.config_spec("batched")          # exactly 1536 prefill tokens
+    pl = _spec_lists(spec)
+    info = pl.info()
+    q = info["prefill_quarters_per_cu"]
+    fused = pl.export(0).reshape(-1, P_F)
+    seq = pl.export(3).reshape(-1, P_F)
+    tiles = len({(int(r[0]), int(r[1])) for r in fused})
+    coloc_slots = max(1, 256 * q // 4)
+    assert len(fused) <= max(tiles, 2 * coloc_slots) + tiles   # per-tile rounding
+    assert len(seq) >= len(fused)
+    # above 1536 tokens the cap uses every slot
+    big = inputs.custom_spec("big", 32, 8, [(1600, 4096)], [2000] * 64, seed=3)
+    pb = _spec_lists(big)
+    assert pb.info()["prefill_items"] == len(pb.export(3)) // P_F
+
+
+def test_proportional_mix():
+    q = {n: _spec_lists(inputs.config_spec(n)).info()["prefill_quarters_per_cu"]
+         for n in inputs.CONFIG_NAMES}
+    assert q["llama2_7b"] <= 2              # decode-heavy MHA: small prefill share
+    assert q["l70b_tp1"] >= 3               # large prefill: about half or more
+    assert 1 <= q["llama3_8b"] <= 7
+    only_p = inputs.custom_spec("p", 8, 8, [(256, 512)], [], seed=1)
+    only_d = inputs.custom_spec("d", 8, 8, [], [512], seed=1)
+    assert _spec_lists(only_p).info()["prefill_quarters_per_cu"] == 8
+    assert _spec_lists(only_d).info()["prefill_quarters_per_cu"] == 0
+    assert _spec_lists(only_p, prefill_quarters_per_cu=3).info()["prefill_quarters_per_cu"] == 3
+
+
+def test_decode_items_longest_first_and_pools_by_kv_head():
+    spec = inputs.config_spec("l70b_tp1")
+    pl = _spec_lists(spec)
+    D = pl.export(1).reshape(-1, D_F)
+    work = D[:, 4] - D[:, 3]
+    assert np.all(np.diff(work) <= 0)
+    P = pl.export(0).reshape(-1, P_F)
+    po = pl.export(6)
+    g = spec.num_qo_heads // spec.num_kv_heads
+    for x in range(len(po) - 1):
+        kvh = set((P[po[x]:po[x + 1], 1] // g).tolist())
+        assert kvh == {x}, (x, kvh)           # 8 KV heads -> one per XCD pool
