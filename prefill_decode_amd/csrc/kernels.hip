@@ -48,31 +48,66 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
 
-// LDS geometry (elements of 16 bits).
-constexpr int kKStr = kHeadDim + 8;          // prefill K tile row: 64 keys x 136
-constexpr int kVtStr = kPrefillKeys + 4;     // prefill V^T tile row: 128 d x 68
-constexpr int kKTileElems = kPrefillKeys * kKStr;
-constexpr int kVtTileElems = kHeadDim * kVtStr;
-constexpr int kPrefillBufElems = kKTileElems + kVtTileElems;
-constexpr int kPrefillLdsBytes = 2 * kPrefillBufElems * 2;          // 69632
-constexpr int kDecVtStr = kDecodeStep + 8;   // decode V^T slice row: 128 d x 40
-constexpr int kDecWaveElems = kHeadDim * kDecVtStr;
-constexpr int kDecodeLdsBytes = kWavesPerWG * kDecWaveElems * 2;    // 40960
+// LDS geometry.  K and V tiles are kept row-major ([key][128 d], 256-byte
+// rows) exactly as LDS DMA deposits them; the 16-byte chunks of each row are
+// XOR-swizzled with bits of the row index (the DMA source addresses carry the
+// swizzle) so that the MFMA-operand reads -- ds_read_b128 for K and the
+// transposing ds_read_b64_tr_b16 for V^T -- are free of bank conflicts.
+constexpr int kRowBytes = kHeadDim * 2;                      // 256
+constexpr int kTileBytes = kPrefillKeys * kRowBytes;         // 16384
+constexpr int kPrefillLdsBytes = 4 * kTileBytes;             // 2 K + 2 V tiles
+constexpr int kDecStepBytes = kDecodeStep * kRowBytes;       // 8192
+constexpr int kDecWaveBytes = 2 * kDecStepBytes;             // V of two steps
+constexpr int kDecodeLdsBytes = kWavesPerWG * kDecWaveBytes; // 65536
 constexpr int kFusedLdsBytes =
     kPrefillLdsBytes > kDecodeLdsBytes ? kPrefillLdsBytes : kDecodeLdsBytes;
+constexpr uint32_t kVSwz = 0xC862EA40u;   // V chunk swizzle by row & 7 (nibble table)
+
+typedef const __attribute__((address_space(4))) int32_t* cptr;   // read-only, scalar-loadable
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int kswz(int r) { return r & 15; }
+__device__ __forceinline__ int vswz(int r) { return (int)((kVSwz >> (4 * (r & 7))) & 15u); }
 
 __device__ __forceinline__ bf16x8 as_bf(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ float fmax_(float a, float b) { return __builtin_fmaxf(a, b); }
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_(float x) { return __builtin_amdgcn_logf(x); }
-__device__ __forceinline__ float xor_shfl(float v, int m) { return __shfl_xor(v, m, 64); }
+// value combined with the same lane of the other 32-lane half (v_permlane32_swap)
+__device__ __forceinline__ float max_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmax_(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// ... and with the other 16-lane row of each 32-lane half (v_permlane16_swap)
+__device__ __forceinline__ float max_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmax_(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ bool any_lane(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 __device__ __forceinline__ void lds_fence() {
   // LDS accesses of one wavefront execute in order; this keeps the compiler
-  // from moving LDS reads above the writes of other lanes.
+  // from moving LDS accesses across each other here.
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+// s_waitcnt vmcnt(N): this wave's vector-memory operations (loads and LDS
+// DMA) issued before the last N have completed.  gfx9 encoding: vmcnt[3:0],
+// expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]; the other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -82,12 +117,30 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   r[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, r);
 }
-// low 16-bit halves of (a, b) -> (a.lo | b.lo << 16); high halves likewise
-__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+
+// Buffer resource over a uniform base (raw, 32-bit byte offsets).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF,
+                                           0x00020000);
 }
-__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x4 gload(const char* p) { return *(const u32x4*)p; }
+// LDS DMA: lane L's 16 bytes at base + voff + soff land at lds_dst + 16 L
+// (lds_dst uniform across the wave)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)lds_dst, 16, voff, soff, 0, 0);
+}
+// ds_read_b64_tr_b16: in each 16-lane group, lane i receives element
+// (i & 3) of the 4-element reads of lanes 4e + (i >> 2), e = 0..3; with lane x
+// reading row k0 + (x >> 2), columns c0 + 4 (x & 3) .. +3 of a row-major
+// [k][c] tile, lane i gets column c0 + i of rows k0 .. k0 + 3.
+__device__ __forceinline__ u32x2 tr_read(const char* p) {
+  const v4s t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(const_cast<char*>(p)));
+  return __builtin_bit_cast(u32x2, t);
 }
 
 // ---------------------------------------------------------------------------
@@ -95,50 +148,59 @@ __device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
 // ---------------------------------------------------------------------------
 template <int KVM>
 struct KvAddr {
-  const int32_t* pages;   // page_indices + page_indptr[req] (paged)
+  cptr pages;             // page_indices + page_indptr[req] (paged)
   int64_t base;           // kv_indptr[req] (contiguous)
   int shift;
   __device__ __forceinline__ void init(const KernelArgs& a, int kvreq) {
     if (KVM == KV_CONTIG) {
-      base = a.kv_indptr[kvreq];
+      base = ((cptr)a.kv_indptr)[kvreq];
       pages = nullptr;
     } else {
       base = 0;
-      pages = a.page_indices + a.page_indptr[kvreq];
+      pages = (cptr)a.page_indices + ((cptr)a.page_indptr)[kvreq];
     }
     shift = a.page_shift;
   }
-  // generic per-lane lookup (any page size)
+  // row of the first token of a 16-key block [t0, t0 + 16) that lies in one
+  // page (page_size >= 16) or in the contiguous layout; uniform (scalar)
+  __device__ __forceinline__ int64_t block_row(int t0) const {
+    if (KVM == KV_CONTIG) return base + t0;
+    const int pg = pages[t0 >> shift];
+    return ((int64_t)pg << shift) + (t0 & ((1 << shift) - 1));
+  }
+  // generic per-lane row of token t
   __device__ __forceinline__ int64_t row(int t) const {
     if (KVM == KV_CONTIG) return base + t;
     const int pg = pages[t >> shift];
     return ((int64_t)pg << shift) + (t & ((1 << shift) - 1));
   }
-  // row of token t0 + i where [t0, t0 + 16) is 16-aligned and lies in one
-  // page (page_size >= 16); `pg` is that page's index (uniform)
-  __device__ __forceinline__ int64_t row_in(int pg, int t0, int i) const {
-    return ((int64_t)pg << shift) + (t0 & ((1 << shift) - 1)) + i;
-  }
 };
 
 // ---------------------------------------------------------------------------
-// Prefill: 128 query rows x one head over keys [kv_begin, kv_end).
+// Prefill: 128 query rows x one head over keys [kv_begin, kv_end), 64-key
+// tiles.  Iteration t: LDS DMA of K(t+1) and V(t) is issued, S(t) = K(t) Q^T
+// runs on the matrix cores, then O^T += V^T(t-1) P^T(t-1) (deferred one
+// tile, so that these MFMAs overlap the softmax of tile t on the VALU).
 // ---------------------------------------------------------------------------
 template <int KVM>
-__device__ __forceinline__ void prefill_tile(const KernelArgs& a, const int32_t* it,
-                                             uint16_t* lds) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+__device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char* lds) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = rfl(tid >> 6);
   const int hl = lane >> 5;            // half of the wave
   const int l32 = lane & 31;
-  const int qrow0 = rfl(it[P_QROW0]), head = rfl(it[P_HEAD]), nrows = rfl(it[P_NROWS]);
-  const int pos0 = rfl(it[P_POS0]), kv_begin = rfl(it[P_KV_BEGIN]), kv_end = rfl(it[P_KV_END]);
-  const int kvreq = rfl(it[P_KVREQ]), part = rfl(it[P_PART]);
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int qrow0 = it[P_QROW0], head = it[P_HEAD], nrows = it[P_NROWS];
+  const int pos0 = it[P_POS0], kv_begin = it[P_KV_BEGIN], kv_end = it[P_KV_END];
+  const int kvreq = it[P_KVREQ], part = it[P_PART];
   const int kvh = head / a.group;
-  const int64_t tok_stride = (int64_t)a.hkv * kHeadDim;
-  const uint16_t* kg = a.k + kvh * kHeadDim;
-  const uint16_t* vg = a.v + kvh * kHeadDim;
+  const uint32_t tok = (uint32_t)a.hkv * kRowBytes;
+  const char* kbase = (const char*)a.k + kvh * kRowBytes;
+  const char* vbase = (const char*)a.v + kvh * kRowBytes;
   KvAddr<KVM> addr;
   addr.init(a, kvreq);
+  const int span = kv_end - kv_begin;
+  const int ntiles = (span + kPrefillKeys - 1) / kPrefillKeys;
+  const int nfull = span / kPrefillKeys;
 
   // Q^T operand: lane holds row (wave*32 + l32), d = 16*kk + 8*hl + e
   const int row = wave * 32 + l32;
@@ -152,156 +214,146 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, const int32_t*
       qf[kk] = row_ok ? *(const u32x4*)(qp + 16 * kk) : u32x4{0, 0, 0, 0};
   }
 
-  // staging assignment: K chunk (key = (tid>>4) + 16 i, d = 8*(tid&15));
-  // V quad (keys 4*(tid&15) + i, d = 8*(tid>>4))
-  const int kc_key = tid >> 4, kc_d = 8 * (tid & 15);
-  const int vq_key = 4 * (tid & 15), vq_d = 8 * (tid >> 4);
-  u32x4 kr[4], vr[4];
-
-  auto load_tile = [&](int k0) {
-    int pg[4];
-    if (KVM == KV_PAGED_WIDE) {
+  // staging: wave w fills rows [16w, 16w + 16) of a tile, four rows per
+  // instruction; lane L deposits row 4i + L/16, chunk position L%16, which
+  // holds source chunk (L%16) ^ swizzle(row)
+  const int dq = lane >> 4, dc = lane & 15;
+  uint32_t voffk[4], voffv[2];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int t = k0 + 16 * b;
-        pg[b] = t < kv_end ? addr.pages[t >> addr.shift] : 0;
+  for (int i = 0; i < 4; ++i) voffk[i] = dq * tok + 16u * (dc ^ kswz(4 * i + dq));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) voffv[i] = dq * tok + 16u * (dc ^ vswz(4 * i + dq));
+  char* const kb0 = lds;
+  char* const vb0 = lds + 2 * kTileBytes;
+  auto ktile = [&](int t) { return kb0 + (t & 1) * kTileBytes; };
+  auto vtile = [&](int t) { return vb0 + (t & 1) * kTileBytes; };
+  auto stage = [&](int t, bool is_k) {
+    const char* gbase = is_k ? kbase : vbase;
+    char* dst = (is_k ? ktile(t) : vtile(t)) + 16 * wave * kRowBytes;
+    const int k0 = kv_begin + t * kPrefillKeys + 16 * wave;
+    if (KVM != KV_PAGED_NARROW && t < nfull) {
+      const auto r = rsrc(gbase + addr.block_row(k0) * tok);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dma16(r, dst + 4 * i * kRowBytes, is_k ? voffk[i] : voffv[i & 1], 4 * i * tok);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rt = 16 * wave + 4 * i + dq;                // row in the tile
+        const int key = min(k0 + 4 * i + dq, kv_end - 1);     // clamp: finite, never read past
+        const int c = dc ^ (is_k ? kswz(rt) : vswz(rt));
+        *(u32x4*)(dst + 4 * i * kRowBytes + 16 * lane) =
+            gload(gbase + addr.row(key) * tok + 16 * c);
       }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kc_key + 16 * i, t = k0 + key;
-      int64_t r;
-      if (KVM == KV_PAGED_WIDE) r = addr.row_in(pg[i], k0 + 16 * i, kc_key);
-      else r = t < kv_end ? addr.row(t) : 0;
-      kr[i] = t < kv_end ? *(const u32x4*)(kg + r * tok_stride + kc_d) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = vq_key + i, t = k0 + key;
-      int64_t r;
-      if (KVM == KV_PAGED_WIDE) r = addr.row_in(pg[key >> 4], k0 + (key & ~15), key & 15);
-      else r = t < kv_end ? addr.row(t) : 0;
-      vr[i] = t < kv_end ? *(const u32x4*)(vg + r * tok_stride + vq_d) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_tile = [&](uint16_t* buf) {
-    uint16_t* ks = buf;
-    uint16_t* vt = buf + kKTileElems;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)(ks + (kc_key + 16 * i) * kKStr + kc_d) = kr[i];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const u32x2 lo = {lo_halves(vr[0][w], vr[1][w]), lo_halves(vr[2][w], vr[3][w])};
-      const u32x2 hi = {hi_halves(vr[0][w], vr[1][w]), hi_halves(vr[2][w], vr[3][w])};
-      *(u32x2*)(vt + (vq_d + 2 * w) * kVtStr + vq_key) = lo;
-      *(u32x2*)(vt + (vq_d + 2 * w + 1) * kVtStr + vq_key) = hi;
-    }
   };
 
-  f32x16 o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
-  float m_run = kNegInf, l_run = 0.0f;
-  const int qpos = pos0 + row;                      // this lane's query position
   const int wave_pos_lo = pos0 + wave * 32;         // smallest position of the wave
   const int wave_pos_hi = wave_pos_lo + 31;
-  const float sl2 = a.scale_log2;
+  const int qpos = pos0 + row;                      // this lane's query position
   const bool causal = a.causal != 0;
+  const float sl2 = a.scale_log2;
+  auto active = [&](int t) { return !causal || kv_begin + t * kPrefillKeys <= wave_pos_hi; };
 
-  const int ntiles = (kv_end - kv_begin + kPrefillKeys - 1) / kPrefillKeys;
-  load_tile(kv_begin);
-  store_tile(lds);
-  if (ntiles > 1) load_tile(kv_begin + kPrefillKeys);
-
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    const uint16_t* buf = lds + (t & 1) * kPrefillBufElems;
-    if (t + 1 < ntiles) {
-      store_tile(lds + ((t + 1) & 1) * kPrefillBufElems);
-      if (t + 2 < ntiles) load_tile(kv_begin + (t + 2) * kPrefillKeys);
-    }
-    const int k0 = kv_begin + t * kPrefillKeys;
-    // whole tile in the future of every row of this wave: nothing to do
-    if (causal && k0 > wave_pos_hi) continue;
-    const uint16_t* ks = buf;
-    const uint16_t* vt = buf + kKTileElems;
-
-    // S^T[key][query] for two 32-key blocks
-    f32x16 s[2];
+  // S^T[key][query] of a tile: A = K rows (key 32 sb + l32), B = Q^T
+  const int ksw = kswz(l32);
+  auto qk = [&](const char* kt, f32x16 (&s)[2]) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
+      const char* rp = kt + (32 * sb + l32) * kRowBytes;
+      f32x16 acc = {};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[sb][r] = 0.0f;
-      const uint16_t* kp = ks + (32 * sb + l32) * kKStr + 8 * hl;
+      for (int kk = 0; kk < 8; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf(*(const u32x4*)(rp + 16 * ((2 * kk + hl) ^ ksw))), as_bf(qf[kk]), acc, 0, 0, 0);
+      s[sb] = acc;
+    }
+  };
+  // O^T += V^T P^T: A = V^T via transposing reads (d = 32 db + l32), B = P^T
+  const int vrow0 = 4 * hl + (j16 >> 2);
+  const int vsw = vswz(vrow0);
+  f32x16 o[4];
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const u32x4 kf = *(const u32x4*)(kp + 16 * kk);
-        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kf), as_bf(qf[kk]), s[sb], 0, 0, 0);
+  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+  auto pv = [&](const char* vt, const u32x4 (&pb)[4]) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int c = 4 * db + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+      const char* cp = vt + 16 * (c ^ vsw) + 8 * (j16 & 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int r0 = 32 * (kk >> 1) + 16 * (kk & 1) + vrow0;
+        const u32x2 lo = tr_read(cp + r0 * kRowBytes);
+        const u32x2 hi = tr_read(cp + (r0 + 8) * kRowBytes);
+        const u32x4 af = {lo[0], lo[1], hi[0], hi[1]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(af), as_bf(pb[kk]), o[db], 0, 0, 0);
       }
     }
-    // mask (only where the tile crosses the split end or the diagonal)
-    const bool need_mask = (k0 + kPrefillKeys > kv_end) ||
-                           (causal && k0 + kPrefillKeys - 1 > wave_pos_lo);
+  };
+
+  float m_run = kNegInf, l_run = 0.0f;
+  // softmax of tile t (lane: one query row, 32 keys) -> P^T operands
+  auto softmax = [&](int t, f32x16 (&s)[2], u32x4 (&pb)[4]) {
+    const int k0 = kv_begin + t * kPrefillKeys;
+    if (t >= nfull || (causal && k0 + kPrefillKeys - 1 > wave_pos_lo)) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * sb + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (key >= kv_end || (causal && key > qpos)) s[sb][r] = kNegInf;
+        }
+    }
     float mx = kNegInf;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[sb][r] * sl2;
-        if (need_mask) {
-          const int key = k0 + 32 * sb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key >= kv_end || (causal && key > qpos)) x = kNegInf;
-        }
-        s[sb][r] = x;
-        mx = fmax_(mx, x);
-      }
-    mx = fmax_(mx, xor_shfl(mx, 32));
-    const float m_new = fmax_(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.0f : m_new;
-    const float alpha = exp2_(m_run - m_use);
-    m_run = m_new;
-    float lsum = 0.0f;
+      for (int r = 0; r < 16; ++r) mx = fmax_(mx, s[sb][r]);
+    mx = max_x32(mx);
+    const float m_new = fmax_(m_run, mx * sl2);
+    if (any_lane(m_new > m_run)) {         // rescale only when a row max grows
+      const float alpha = exp2_(m_run - (m_new == kNegInf ? 0.0f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float nm = m_run == kNegInf ? 0.0f : -m_run;
+    float ls = 0.0f;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2_(s[sb][r] - m_use);
+        const float p = exp2_(__builtin_fmaf(s[sb][r], sl2, nm));
         s[sb][r] = p;
-        lsum += p;
+        ls += p;
       }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-
+    l_run += ls;
     // P^T operands: k-step kk uses block kk>>1, registers 8*(kk&1) .. +7
-    u32x4 pb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         pb[kk][e] = pack_bf16x2(s[kk >> 1][8 * (kk & 1) + 2 * e],
                                 s[kk >> 1][8 * (kk & 1) + 2 * e + 1]);
-    // O^T[d][query] += V^T[d][key] P^T[key][query]
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const uint16_t* vrow = vt + (32 * db + l32) * kVtStr + 4 * hl;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int ko = 32 * (kk >> 1) + 16 * (kk & 1);
-        const u32x2 v0 = *(const u32x2*)(vrow + ko);
-        const u32x2 v1 = *(const u32x2*)(vrow + ko + 8);
-        const u32x4 af = {v0[0], v0[1], v1[0], v1[1]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(af), as_bf(pb[kk]), o[db], 0, 0, 0);
-      }
-    }
+  };
+
+  f32x16 s[2];
+  u32x4 pb[4];
+  stage(0, true);
+  for (int t = 0; t <= ntiles; ++t) {
+    wait_vmem<0>();
+    __syncthreads();                       // K(t), V(t-1) in LDS; K(t-1), V(t-2) consumed
+    if (t + 1 < ntiles) stage(t + 1, true);
+    if (t < ntiles) stage(t, false);
+    const bool act = t < ntiles && active(t);
+    if (act) qk(ktile(t), s);
+    if (t >= 1 && active(t - 1)) pv(vtile(t - 1), pb);
+    if (act) softmax(t, s, pb);
   }
 
   // epilogue: lanes l and l^32 hold the same query row
-  const float l_tot = l_run + xor_shfl(l_run, 32);
+  const float l_tot = sum_x32(l_run);
   if (!row_ok) return;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse2 = l_tot > 0.0f ? m_run + log2_(l_tot) : kNegInf;
@@ -333,22 +385,27 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, const int32_t*
 }
 
 // ---------------------------------------------------------------------------
-// Decode: one wavefront, <=16 query heads sharing a KV head, keys [kb, ke).
+// Decode: one wavefront, <=16 query heads sharing a KV head, keys [kb, ke),
+// 32 keys per step.  K goes straight from HBM into MFMA operand registers; V
+// goes by LDS DMA into the wave's double-buffered slice and is read back
+// transposed.  The loads of step s+1 are in flight while step s computes.
 // ---------------------------------------------------------------------------
 template <int KVM>
-__device__ __forceinline__ void decode_unit(const KernelArgs& a, const int32_t* it,
-                                            uint16_t* vt) {
+__device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* wl) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, q4 = lane >> 4;
-  const int qi = rfl(it[D_QROW]), h0 = rfl(it[D_HEAD0]), nq = rfl(it[D_NQ]);
-  const int kb = rfl(it[D_KV_BEGIN]), ke = rfl(it[D_KV_END]), kvreq = rfl(it[D_KVREQ]);
-  const int part = rfl(it[D_PART]), pstride = rfl(it[D_PSTRIDE]);
+  const int qi = it[D_QROW], h0 = it[D_HEAD0], nq = it[D_NQ];
+  const int kb = it[D_KV_BEGIN], ke = it[D_KV_END], kvreq = it[D_KVREQ];
+  const int part = it[D_PART], pstride = it[D_PSTRIDE];
   const int kvh = h0 / a.group;
-  const int64_t tok_stride = (int64_t)a.hkv * kHeadDim;
-  const uint16_t* kg = a.k + kvh * kHeadDim;
-  const uint16_t* vg = a.v + kvh * kHeadDim;
+  const uint32_t tok = (uint32_t)a.hkv * kRowBytes;
+  const char* kbase = (const char*)a.k + kvh * kRowBytes;
+  const char* vbase = (const char*)a.v + kvh * kRowBytes;
   KvAddr<KVM> addr;
   addr.init(a, kvreq);
+  const int span = ke - kb;
+  const int nsteps = (span + kDecodeStep - 1) / kDecodeStep;
+  const int nfull = span / kDecodeStep;
 
   // Q^T operand: lane holds query j (head h0 + j), d = 32*kk + 8*q4 + e
   u32x4 qf[4];
@@ -360,39 +417,44 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, const int32_t* 
       qf[kk] = ok ? *(const u32x4*)(qp + 32 * kk) : u32x4{0, 0, 0, 0};
   }
 
-  // K operand: key k0 + 16*sb + j, d = 32*kk + 8*q4 (register sb*4 + kk)
-  // V rows:    key k0 + 8*q4 + i, d = 8*j .. 8*j+7     (register i)
-  auto load_step = [&](int k0, u32x4 (&kr)[8], u32x4 (&vr)[8]) {
-    int64_t krow[2], vrow0 = 0;
-    if (KVM == KV_PAGED_WIDE) {
-      const int pg0 = addr.pages[k0 >> addr.shift];
-      const int pg1 = k0 + 16 < ke ? addr.pages[(k0 + 16) >> addr.shift] : pg0;
-      krow[0] = addr.row_in(pg0, k0, j);
-      krow[1] = addr.row_in(pg1, k0 + 16, j);
-      vrow0 = addr.row_in(q4 < 2 ? pg0 : pg1, k0 + 16 * (q4 >> 1), 8 * (q4 & 1));
-    } else if (KVM == KV_CONTIG) {
-      krow[0] = addr.base + k0 + j;
-      krow[1] = addr.base + k0 + 16 + j;
-      vrow0 = addr.base + k0 + 8 * q4;
+  // K operand: key k0 + 16*sb + j, bytes 64*kk + 16*q4   (register 4*sb + kk)
+  // V: LDS rows 4i + L/16 (i = 0..7) of the step's slice, chunk L%16
+  const uint32_t voff_k = j * tok + 16u * q4;
+  const int dq = lane >> 4, dc = lane & 15;
+  const uint32_t voffv0 = dq * tok + 16u * (dc ^ vswz(dq));
+  const uint32_t voffv1 = dq * tok + 16u * (dc ^ vswz(4 + dq));
+  auto vbuf = [&](int s) { return wl + (s & 1) * kDecStepBytes; };
+  auto load_step = [&](int s, u32x4 (&kr)[8]) {
+    const int k0 = kb + s * kDecodeStep;
+    char* dst = vbuf(s);
+    if (KVM != KV_PAGED_NARROW && s < nfull) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const int64_t rw = addr.block_row(k0 + 16 * sb);
+        const auto rk = rsrc(kbase + rw * tok);
+        const auto rv = rsrc(vbase + rw * tok);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kr[4 * sb + kk] = bload(rk, voff_k + 64u * kk, 0);
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          dma16(rv, dst + (16 * sb + 4 * i4) * kRowBytes, (i4 & 1) ? voffv1 : voffv0,
+                4 * i4 * tok);
+      }
     } else {
-      krow[0] = k0 + j < ke ? addr.row(k0 + j) : 0;
-      krow[1] = k0 + 16 + j < ke ? addr.row(k0 + 16 + j) : 0;
-    }
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const bool ok = k0 + 16 * sb + j < ke;
-      const uint16_t* p = kg + krow[sb] * tok_stride + 8 * q4;
+      for (int sb = 0; sb < 2; ++sb) {
+        const int tk = min(k0 + 16 * sb + j, ke - 1);      // clamp: finite, never read past
+        const char* pk = kbase + addr.row(tk) * tok + 16 * q4;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        kr[sb * 4 + kk] = ok ? *(const u32x4*)(p + 32 * kk) : u32x4{0, 0, 0, 0};
-    }
+        for (int kk = 0; kk < 4; ++kk) kr[4 * sb + kk] = gload(pk + 64 * kk);
+      }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = k0 + 8 * q4 + i;
-      int64_t r;
-      if (KVM == KV_PAGED_NARROW) r = t < ke ? addr.row(t) : 0;
-      else r = vrow0 + i;
-      vr[i] = t < ke ? *(const u32x4*)(vg + r * tok_stride + 8 * j) : u32x4{0, 0, 0, 0};
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + dq;
+        const int tv = min(k0 + r, ke - 1);
+        *(u32x4*)(dst + 4 * i * kRowBytes + 16 * lane) =
+            gload(vbase + addr.row(tv) * tok + 16 * (dc ^ vswz(r)));
+      }
     }
   };
 
@@ -401,9 +463,13 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, const int32_t* 
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = kNegInf, l_run = 0.0f;
   const float sl2 = a.scale_log2;
+  // V^T read lanes: rows 4*q4 + j/4 (+16), chunk 2 db + (j&3)/2, half j&1
+  const int vrow0 = 4 * q4 + (j >> 2);
+  const int vsw = vswz(vrow0);
 
-  auto compute_step = [&](int k0, const u32x4 (&kr)[8], const u32x4 (&vr)[8]) {
-    f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute_step = [&](int s, const u32x4 (&kr)[8], bool more) {
+    const int k0 = kb + s * kDecodeStep;
+    f32x4 s0 = {}, s1 = {};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(kr[kk]), as_bf(qf[kk]), s0, 0, 0, 0);
@@ -413,10 +479,10 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, const int32_t* 
     float x[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      x[r] = s0[r] * sl2;
-      x[4 + r] = s1[r] * sl2;
+      x[r] = s0[r];
+      x[4 + r] = s1[r];
     }
-    if (k0 + kDecodeStep > ke) {
+    if (s >= nfull) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (k0 + 4 * q4 + r >= ke) x[r] = kNegInf;
@@ -426,63 +492,54 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, const int32_t* 
     float mx = x[0];
 #pragma unroll
     for (int r = 1; r < 8; ++r) mx = fmax_(mx, x[r]);
-    mx = fmax_(mx, xor_shfl(mx, 16));
-    mx = fmax_(mx, xor_shfl(mx, 32));
-    const float m_new = fmax_(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.0f : m_new;
-    const float alpha = exp2_(m_run - m_use);
-    m_run = m_new;
+    mx = max_x32(max_x16(mx));
+    const float m_new = fmax_(m_run, mx * sl2);
+    if (any_lane(m_new > m_run)) {
+      const float alpha = exp2_(m_run - (m_new == kNegInf ? 0.0f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float nm = m_run == kNegInf ? 0.0f : -m_run;
     float ls = 0.0f;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      x[r] = exp2_(x[r] - m_use);
+      x[r] = exp2_(__builtin_fmaf(x[r], sl2, nm));
       ls += x[r];
     }
-    l_run = l_run * alpha + ls;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= alpha;
-
-    // V^T slice: row d = 8*j + 2*w (+1), keys 8*q4 .. 8*q4+7
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const u32x4 lo = {lo_halves(vr[0][w], vr[1][w]), lo_halves(vr[2][w], vr[3][w]),
-                        lo_halves(vr[4][w], vr[5][w]), lo_halves(vr[6][w], vr[7][w])};
-      const u32x4 hi = {hi_halves(vr[0][w], vr[1][w]), hi_halves(vr[2][w], vr[3][w]),
-                        hi_halves(vr[4][w], vr[5][w]), hi_halves(vr[6][w], vr[7][w])};
-      *(u32x4*)(vt + (8 * j + 2 * w) * kDecVtStr + 8 * q4) = lo;
-      *(u32x4*)(vt + (8 * j + 2 * w + 1) * kDecVtStr + 8 * q4) = hi;
-    }
-    lds_fence();
+    l_run += ls;
     // P^T operand: e = 0..3 -> key 4*q4 + e, e = 4..7 -> key 16 + 4*q4 + e - 4
     const u32x4 pb = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
                       pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+    // this step's V must have landed: only the next step's 16 loads may be pending
+    if (more) wait_vmem<16>();
+    else wait_vmem<0>();
+    lds_fence();
+    const char* vt = vbuf(s) + vrow0 * kRowBytes + 8 * (j & 1);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const uint16_t* vrow = vt + (16 * db + j) * kDecVtStr + 4 * q4;
-      const u32x2 v0 = *(const u32x2*)(vrow);
-      const u32x2 v1 = *(const u32x2*)(vrow + 16);
-      const u32x4 af = {v0[0], v0[1], v1[0], v1[1]};
+      const char* cp = vt + 16 * ((2 * db + ((j & 3) >> 1)) ^ vsw);
+      const u32x2 lo = tr_read(cp);
+      const u32x2 hi = tr_read(cp + 16 * kRowBytes);
+      const u32x4 af = {lo[0], lo[1], hi[0], hi[1]};
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(af), as_bf(pb), o[db], 0, 0, 0);
     }
     lds_fence();
   };
 
-  u32x4 ka[8], va[8], kn[8], vn[8];
-  int k0 = kb;
-  if (k0 < ke) load_step(k0, ka, va);
-  while (k0 < ke) {
-    if (k0 + kDecodeStep < ke) load_step(k0 + kDecodeStep, kn, vn);
-    compute_step(k0, ka, va);
-    k0 += kDecodeStep;
-    if (k0 >= ke) break;
-    if (k0 + kDecodeStep < ke) load_step(k0 + kDecodeStep, ka, va);
-    compute_step(k0, kn, vn);
-    k0 += kDecodeStep;
+  u32x4 ka[8], kn[8];
+  if (nsteps > 0) load_step(0, ka);
+  for (int s = 0; s < nsteps; s += 2) {
+    if (s + 1 < nsteps) load_step(s + 1, kn);
+    compute_step(s, ka, s + 1 < nsteps);
+    if (s + 1 >= nsteps) break;
+    if (s + 2 < nsteps) load_step(s + 2, ka);
+    compute_step(s + 1, kn, s + 2 < nsteps);
   }
 
   // epilogue: query j is spread over lanes j, j+16, j+32, j+48
-  float l_tot = l_run + xor_shfl(l_run, 16);
-  l_tot += xor_shfl(l_tot, 32);
+  const float l_tot = sum_x32(sum_x16(l_run));
   if (j >= nq) return;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse2 = l_tot > 0.0f ? m_run + log2_(l_tot) : kNegInf;
@@ -562,7 +619,7 @@ __device__ __forceinline__ void finish_launch(const KernelArgs& a, bool reset_cu
 // ---------------------------------------------------------------------------
 template <int KVM>
 __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
-  extern __shared__ __align__(16) uint16_t lds[];
+  extern __shared__ __align__(16) char lds[];
   __shared__ int s_info[4];
   if (threadIdx.x == 0) {
     const int slot = cu_slot_id();
@@ -621,12 +678,12 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
   const int role = s_info[0], unit = s_info[1];
   if (unit >= 0) {
     if (role == 0) {
-      prefill_tile<KVM>(a, a.p_items + (int64_t)unit * P_FIELDS, lds);
+      prefill_tile<KVM>(a, (cptr)a.p_items + rfl(unit) * P_FIELDS, lds);
     } else {
       const int wave = threadIdx.x >> 6;
       const int d = unit * kWavesPerWG + wave;
       if (d < a.n_d)
-        decode_unit<KVM>(a, a.d_items + (int64_t)d * D_FIELDS, lds + wave * kDecWaveElems);
+        decode_unit<KVM>(a, (cptr)a.d_items + rfl(d) * D_FIELDS, lds + rfl(wave) * kDecWaveBytes);
     }
   }
   __syncthreads();
@@ -640,22 +697,22 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
 
 template <int KVM>
 __global__ __launch_bounds__(256, 2) void pod_prefill_kernel(KernelArgs a) {
-  extern __shared__ __align__(16) uint16_t lds[];
+  extern __shared__ __align__(16) char lds[];
   __shared__ int s_info[2];
   if (threadIdx.x == 0) s_info[0] = claim_prefill(a, cu_slot_id() >> 8);
   __syncthreads();
   const int unit = s_info[0];
-  if (unit >= 0) prefill_tile<KVM>(a, a.p_items + (int64_t)unit * P_FIELDS, lds);
+  if (unit >= 0) prefill_tile<KVM>(a, (cptr)a.p_items + rfl(unit) * P_FIELDS, lds);
   finish_launch(a, false, &s_info[1]);
 }
 
 template <int KVM>
 __global__ __launch_bounds__(256, 2) void pod_decode_kernel(KernelArgs a) {
-  extern __shared__ __align__(16) uint16_t lds[];
+  extern __shared__ __align__(16) char lds[];
   const int wave = threadIdx.x >> 6;
   const int d = blockIdx.x * kWavesPerWG + wave;
   if (d < a.n_d)
-    decode_unit<KVM>(a, a.d_items + (int64_t)d * D_FIELDS, lds + wave * kDecWaveElems);
+    decode_unit<KVM>(a, (cptr)a.d_items + rfl(d) * D_FIELDS, lds + rfl(wave) * kDecWaveBytes);
 }
 
 __global__ __launch_bounds__(256) void pod_merge_kernel(KernelArgs a) {

@@ -1,0 +1,48 @@
+"""Algorithmic FLOP and byte counts of one hybrid batch (for the roofline).
+
+Counts each Q, K, V, O and LSE byte once (K/V once per KV head), page
+indices as int32, and only the visible (query, key) pairs:
+
+    pairs(prefill r) = qo*(kv - qo) + qo*(qo + 1)/2   (causal; qo*kv otherwise)
+    pairs(decode r)  = kv
+    FLOPs            = 4 * d * Hq * sum(pairs)        (QK^T and PV, 2 flops/MAC)
+
+Re-reads of K/V by several prefill tiles, split partials, masked MFMA work on
+diagonal tiles and the padding of decode rows to 16 are overheads, not counted.
+"""
+
+import numpy as np
+
+PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E, B/s
+
+
+def algorithmic_counts(b) -> dict:
+    get = (lambda k: getattr(b, k)) if not isinstance(b, dict) else (lambda k: b[k])
+    hq, hkv, d = get("num_qo_heads"), get("num_kv_heads"), get("head_dim")
+    qo = np.asarray(get("prefill_qo_len"), dtype=np.float64)
+    pkv = np.asarray(get("prefill_kv_len"), dtype=np.float64)
+    dkv = np.asarray(get("decode_kv_len"), dtype=np.float64)
+    causal = bool(get("causal"))
+    pairs_p = float(np.sum(qo * (pkv - qo) + qo * (qo + 1) / 2)) if causal \
+        else float(np.sum(qo * pkv))
+    pairs_d = float(np.sum(dkv))
+    paged = get("layout") == "paged"
+    ps = get("page_size")
+    rows_p, rows_d = float(np.sum(qo)), float(len(dkv))
+
+    def part_bytes(rows, kv_tokens, pages):
+        qo_b = rows * hq * d * 2 * 2 + rows * hq * 4          # Q + O (bf16) + LSE
+        kv_b = kv_tokens * hkv * d * 2 * 2                    # K + V (bf16)
+        return qo_b + kv_b + (pages * 4 if paged else 0.0)
+
+    bp = part_bytes(rows_p, float(np.sum(pkv)), float(np.sum(np.ceil(pkv / ps))))
+    bd = part_bytes(rows_d, float(np.sum(dkv)), float(np.sum(np.ceil(dkv / ps))))
+    fp = 4.0 * d * hq * pairs_p
+    fd = 4.0 * d * hq * pairs_d
+    return {"flops": fp + fd, "bytes": bp + bd, "flops_prefill": fp, "flops_decode": fd,
+            "bytes_prefill": bp, "bytes_decode": bd}
+
+
+def overlap_roofline_s(c: dict) -> float:
+    return max(c["flops"] / PEAK_BF16_FLOPS, c["bytes"] / PEAK_HBM_BYTES)
