@@ -32,7 +32,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <mutex>
+#include <type_traits>
 
 #include "kernel_args.h"
 #include "plan.h"
@@ -55,12 +55,15 @@ constexpr float kLn2 = 0.693147180559945309f;
 // transposing ds_read_b64_tr_b16 for V^T -- are free of bank conflicts.
 constexpr int kRowBytes = kHeadDim * 2;                      // 256
 constexpr int kTileBytes = kPrefillKeys * kRowBytes;         // 16384
-constexpr int kPrefillLdsBytes = 4 * kTileBytes;             // 2 K + 2 V tiles
 constexpr int kDecStepBytes = kDecodeStep * kRowBytes;       // 8192
-constexpr int kDecWaveBytes = 2 * kDecStepBytes;             // V of two steps
-constexpr int kDecodeLdsBytes = kWavesPerWG * kDecWaveBytes; // 65536
-constexpr int kFusedLdsBytes =
-    kPrefillLdsBytes > kDecodeLdsBytes ? kPrefillLdsBytes : kDecodeLdsBytes;
+// A workgroup owns two LDS objects of 32 KiB (64 KiB in all, so two
+// workgroups fit a CU's 160 KiB): X = {K tile 0, V tile 1}, Y = {K tile 1,
+// V tile 0}.  In each prefill iteration the DMAs fill one object while the
+// MFMA operands are read from the other; decode wave w keeps its step buffers
+// of parity 0 / 1 at X + 8w KiB / Y + 8w KiB.  Because the buffers being
+// filled and the buffers being read are distinct objects, the compiler can
+// prove that an LDS DMA in flight does not alias the reads and adds no wait
+// for it.
 constexpr uint32_t kVSwz = 0xC862EA40u;   // V chunk swizzle by row & 7 (nibble table)
 
 typedef const __attribute__((address_space(4))) int32_t* cptr;   // read-only, scalar-loadable
@@ -94,13 +97,11 @@ __device__ __forceinline__ float sum_x16(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ __forceinline__ bool any_lane(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
-__device__ __forceinline__ void lds_fence() {
-  // LDS accesses of one wavefront execute in order; this keeps the compiler
-  // from moving LDS accesses across each other here.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+// Compiler-only barrier for one wavefront's LDS traffic.  The hardware keeps
+// one wave's LDS instructions in order and s_waitcnt covers LDS DMA, so no
+// machine wait is needed; a memory fence here would also wait for the LDS DMA
+// of the next step, which is still meant to be in flight.
+__device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
 // s_waitcnt vmcnt(N): this wave's vector-memory operations (loads and LDS
 // DMA) issued before the last N have completed.  gfx9 encoding: vmcnt[3:0],
 // expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]; the other counters untouched.
@@ -123,15 +124,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF,
                                            0x00020000);
 }
+// cache policy bits of buffer loads: 0 = default, kStream = non-temporal
+// (data read once, e.g. a decode request's KV, should not displace reused lines)
+constexpr int kStream = 2;
+template <int CP = 0>
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, CP));
 }
 __device__ __forceinline__ u32x4 gload(const char* p) { return *(const u32x4*)p; }
 // LDS DMA: lane L's 16 bytes at base + voff + soff land at lds_dst + 16 L
 // (lds_dst uniform across the wave)
+template <int CP = 0>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff,
                                       uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)lds_dst, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)lds_dst, 16, voff, soff, 0, CP);
 }
 // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element
 // (i & 3) of the 4-element reads of lanes 4e + (i >> 2), e = 0..3; with lane x
@@ -181,9 +187,13 @@ struct KvAddr {
 // tiles.  Iteration t: LDS DMA of K(t+1) and V(t) is issued, S(t) = K(t) Q^T
 // runs on the matrix cores, then O^T += V^T(t-1) P^T(t-1) (deferred one
 // tile, so that these MFMAs overlap the softmax of tile t on the VALU).
+// The loop is unrolled by two so that every LDS address is a per-lane base
+// plus an immediate offset.
 // ---------------------------------------------------------------------------
 template <int KVM>
-__device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char* lds) {
+__device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char* __restrict__ kt0,
+                                             char* __restrict__ kt1, char* __restrict__ vt0,
+                                             char* __restrict__ vt1) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = rfl(tid >> 6);
   const int hl = lane >> 5;            // half of the wave
@@ -201,10 +211,20 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   const int span = kv_end - kv_begin;
   const int ntiles = (span + kPrefillKeys - 1) / kPrefillKeys;
   const int nfull = span / kPrefillKeys;
+  const bool causal = a.causal != 0;
+  const float sl2 = a.scale_log2;
+  const int wave_pos_lo = pos0 + wave * 32;         // smallest position of the wave
+  // tiles [0, t_act) hold a key visible to some row of this wave; tiles
+  // >= t_mask need per-element masking (split end or diagonal)
+  const int x_act = wave_pos_lo + 31 - kv_begin;
+  const int t_act = !causal ? ntiles : x_act < 0 ? 0 : min(ntiles, x_act / kPrefillKeys + 1);
+  const int t_mask = causal ? min(nfull, max(0, (wave_pos_lo - kv_begin + 1) / kPrefillKeys))
+                            : nfull;
 
   // Q^T operand: lane holds row (wave*32 + l32), d = 16*kk + 8*hl + e
   const int row = wave * 32 + l32;
   const bool row_ok = row < nrows;
+  const int qpos = pos0 + row;                      // this lane's query position
   u32x4 qf[8];
   {
     const uint16_t* qp = a.q_prefill +
@@ -223,20 +243,32 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   for (int i = 0; i < 4; ++i) voffk[i] = dq * tok + 16u * (dc ^ kswz(4 * i + dq));
 #pragma unroll
   for (int i = 0; i < 2; ++i) voffv[i] = dq * tok + 16u * (dc ^ vswz(4 * i + dq));
-  char* const kb0 = lds;
-  char* const vb0 = lds + 2 * kTileBytes;
-  auto ktile = [&](int t) { return kb0 + (t & 1) * kTileBytes; };
-  auto vtile = [&](int t) { return vb0 + (t & 1) * kTileBytes; };
-  auto stage = [&](int t, bool is_k) {
-    const char* gbase = is_k ? kbase : vbase;
-    char* dst = (is_k ? ktile(t) : vtile(t)) + 16 * wave * kRowBytes;
-    const int k0 = kv_begin + t * kPrefillKeys + 16 * wave;
-    if (KVM != KV_PAGED_NARROW && t < nfull) {
-      const auto r = rsrc(gbase + addr.block_row(k0) * tok);
+  const int wrow = 16 * wave * kRowBytes;           // this wave's rows in a tile
+  // A tile's 16-key blocks each lie in one page (page_size >= 16); in the
+  // last, partial tile the blocks and the lanes' rows are clamped to the last
+  // key (finite data, never read past it).
+  const int lastb = (kv_end - 1) & ~15;             // start of the block holding key kv_end-1
+  auto bstart = [&](int t) { return min(kv_begin + t * kPrefillKeys + 16 * wave, lastb); };
+  auto stage = [&](int t, bool is_k, int buf, __amdgpu_buffer_rsrc_t r) {
+    char* dst = (is_k ? (buf ? kt1 : kt0) : (buf ? vt1 : vt0)) + wrow;
+    if (KVM != KV_PAGED_NARROW) {
+      const int rmax = kv_end - 1 - bstart(t);
+      if (rmax >= 15) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dma16(r, dst + 4 * i * kRowBytes, is_k ? voffk[i] : voffv[i & 1], 4 * i * tok);
+        for (int i = 0; i < 4; ++i)
+          dma16(r, dst + 4 * i * kRowBytes, is_k ? voffk[i] : voffv[i & 1], 4 * i * tok);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 4 * i + dq;
+          const uint32_t vo = (uint32_t)min(rr, rmax) * tok +
+                              16u * (dc ^ (is_k ? kswz(rr) : vswz(rr)));
+          dma16(r, dst + 4 * i * kRowBytes, vo, 0);
+        }
+      }
     } else {
+      const char* gbase = is_k ? kbase : vbase;
+      const int k0 = kv_begin + t * kPrefillKeys + 16 * wave;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rt = 16 * wave + 4 * i + dq;                // row in the tile
@@ -247,42 +279,52 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
       }
     }
   };
-
-  const int wave_pos_lo = pos0 + wave * 32;         // smallest position of the wave
-  const int wave_pos_hi = wave_pos_lo + 31;
-  const int qpos = pos0 + row;                      // this lane's query position
-  const bool causal = a.causal != 0;
-  const float sl2 = a.scale_log2;
-  auto active = [&](int t) { return !causal || kv_begin + t * kPrefillKeys <= wave_pos_hi; };
-
-  // S^T[key][query] of a tile: A = K rows (key 32 sb + l32), B = Q^T
-  const int ksw = kswz(l32);
-  auto qk = [&](const char* kt, f32x16 (&s)[2]) {
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const char* rp = kt + (32 * sb + l32) * kRowBytes;
-      f32x16 acc = {};
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf(*(const u32x4*)(rp + 16 * ((2 * kk + hl) ^ ksw))), as_bf(qf[kk]), acc, 0, 0, 0);
-      s[sb] = acc;
-    }
+  // resource of this wave's (clamped) 16-key block of tile t
+  auto block_rsrc = [&](int t, const char* gbase) {
+    return rsrc(gbase + (KVM != KV_PAGED_NARROW ? addr.block_row(bstart(t)) : 0) * tok);
   };
-  // O^T += V^T P^T: A = V^T via transposing reads (d = 32 db + l32), B = P^T
+
+  // per-lane LDS read offsets (bytes from a tile's base)
+  // K rows 32 sb + l32, chunk (2 kk + hl) ^ swz; sb and the buffer are immediates
+  uint32_t koff[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    koff[kk] = (uint32_t)(l32 * kRowBytes + 16 * ((2 * kk + hl) ^ kswz(l32)));
+  // V^T reads: rows vrow0 + 32 (kk>>1) + 16 (kk&1) (+8), chunk 4 db + .. ^ swz
   const int vrow0 = 4 * hl + (j16 >> 2);
   const int vsw = vswz(vrow0);
+  uint32_t voff[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    voff[db] = (uint32_t)(vrow0 * kRowBytes +
+                          16 * ((4 * db + 2 * (g16 & 1) + ((j16 & 3) >> 1)) ^ vsw) + 8 * (j16 & 1));
+
+  // the two key blocks' accumulation chains are interleaved so that
+  // consecutive MFMAs are independent
+  auto qk = [&](int buf, f32x16 (&s)[2]) {
+    f32x16 a0 = {}, a1 = {};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const char* kp = (buf ? kt1 : kt0) + koff[kk];
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(*(const u32x4*)kp), as_bf(qf[kk]), a0,
+                                                   0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          as_bf(*(const u32x4*)(kp + 32 * kRowBytes)), as_bf(qf[kk]), a1, 0, 0, 0);
+    }
+    s[0] = a0;
+    s[1] = a1;
+  };
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  auto pv = [&](const char* vt, const u32x4 (&pb)[4]) {
+  // four independent accumulation chains (d blocks), interleaved
+  auto pv = [&](int buf, const u32x4 (&pb)[4]) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int c = 4 * db + 2 * (g16 & 1) + ((j16 & 3) >> 1);
-      const char* cp = vt + 16 * (c ^ vsw) + 8 * (j16 & 1);
+    for (int kk = 0; kk < 4; ++kk) {
+      const int r0 = 32 * (kk >> 1) + 16 * (kk & 1);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int r0 = 32 * (kk >> 1) + 16 * (kk & 1) + vrow0;
+      for (int db = 0; db < 4; ++db) {
+        const char* cp = (buf ? vt1 : vt0) + voff[db];
         const u32x2 lo = tr_read(cp + r0 * kRowBytes);
         const u32x2 hi = tr_read(cp + (r0 + 8) * kRowBytes);
         const u32x4 af = {lo[0], lo[1], hi[0], hi[1]};
@@ -294,13 +336,13 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   float m_run = kNegInf, l_run = 0.0f;
   // softmax of tile t (lane: one query row, 32 keys) -> P^T operands
   auto softmax = [&](int t, f32x16 (&s)[2], u32x4 (&pb)[4]) {
-    const int k0 = kv_begin + t * kPrefillKeys;
-    if (t >= nfull || (causal && k0 + kPrefillKeys - 1 > wave_pos_lo)) {
+    if (t >= t_mask) {
+      const int k0 = kv_begin + t * kPrefillKeys + 4 * hl;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * sb + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const int key = k0 + 32 * sb + 8 * (r >> 2) + (r & 3);
           if (key >= kv_end || (causal && key > qpos)) s[sb][r] = kNegInf;
         }
     }
@@ -340,16 +382,29 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
 
   f32x16 s[2];
   u32x4 pb[4];
-  stage(0, true);
-  for (int t = 0; t <= ntiles; ++t) {
+  // iteration t uses K buffer t&1 and V buffer (t-1)&1; `par` = t&1
+  __amdgpu_buffer_rsrc_t rk_next = block_rsrc(0, kbase);
+  __amdgpu_buffer_rsrc_t rv_cur = block_rsrc(0, vbase);
+  stage(0, true, 0, rk_next);
+  auto body = [&](int t, auto par) {
+    constexpr int P = decltype(par)::value;
     wait_vmem<0>();
     __syncthreads();                       // K(t), V(t-1) in LDS; K(t-1), V(t-2) consumed
-    if (t + 1 < ntiles) stage(t + 1, true);
-    if (t < ntiles) stage(t, false);
-    const bool act = t < ntiles && active(t);
-    if (act) qk(ktile(t), s);
-    if (t >= 1 && active(t - 1)) pv(vtile(t - 1), pb);
-    if (act) softmax(t, s, pb);
+    // DMA of K(t+1) and V(t) into the buffers the barrier released; they
+    // have a whole iteration to land
+    if (t + 1 < ntiles) {
+      rk_next = block_rsrc(t + 1, kbase);
+      stage(t + 1, true, P ^ 1, rk_next);
+    }
+    if (t < ntiles) stage(t, false, P, rv_cur);
+    if (t < t_act) qk(P, s);
+    if (t >= 1 && t - 1 < t_act) pv(P ^ 1, pb);
+    if (t < t_act) softmax(t, s, pb);
+    if (t + 1 < ntiles) rv_cur = block_rsrc(t + 1, vbase);
+  };
+  for (int t = 0; t <= ntiles; t += 2) {
+    body(t, std::integral_constant<int, 0>{});
+    if (t + 1 <= ntiles) body(t + 1, std::integral_constant<int, 1>{});
   }
 
   // epilogue: lanes l and l^32 hold the same query row
@@ -391,7 +446,8 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
 // transposed.  The loads of step s+1 are in flight while step s computes.
 // ---------------------------------------------------------------------------
 template <int KVM>
-__device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* wl) {
+__device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* __restrict__ vb0,
+                                            char* __restrict__ vb1) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, q4 = lane >> 4;
   const int qi = it[D_QROW], h0 = it[D_HEAD0], nq = it[D_NQ];
@@ -418,40 +474,54 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
   }
 
   // K operand: key k0 + 16*sb + j, bytes 64*kk + 16*q4   (register 4*sb + kk)
-  // V: LDS rows 4i + L/16 (i = 0..7) of the step's slice, chunk L%16
-  const uint32_t voff_k = j * tok + 16u * q4;
+  // V: LDS rows 4i + L/16 (i = 0..7) of the step's slice, chunk L%16.
+  // A step's two 16-key blocks each lie in one page (page_size >= 16), so each
+  // has one uniform buffer resource; in a unit's last step the blocks and the
+  // lanes' rows are clamped to the last key (finite data, never read past it).
   const int dq = lane >> 4, dc = lane & 15;
-  const uint32_t voffv0 = dq * tok + 16u * (dc ^ vswz(dq));
-  const uint32_t voffv1 = dq * tok + 16u * (dc ^ vswz(4 + dq));
-  auto vbuf = [&](int s) { return wl + (s & 1) * kDecStepBytes; };
-  auto load_step = [&](int s, u32x4 (&kr)[8]) {
-    const int k0 = kb + s * kDecodeStep;
-    char* dst = vbuf(s);
-    if (KVM != KV_PAGED_NARROW && s < nfull) {
+  const int lastb = (ke - 1) & ~15;                 // start of the block holding key ke-1
+  struct Blk { __amdgpu_buffer_rsrc_t rk, rv; int rmax; };
+  auto block = [&](int s, int sb) {
+    const int bs = min(kb + s * kDecodeStep + 16 * sb, lastb);
+    const int64_t rw = addr.block_row(bs);
+    return Blk{rsrc(kbase + rw * tok), rsrc(vbase + rw * tok), ke - 1 - bs};
+  };
+  auto load_k = [&](int s, u32x4 (&kr)[8]) {
+    if (KVM != KV_PAGED_NARROW) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        const int64_t rw = addr.block_row(k0 + 16 * sb);
-        const auto rk = rsrc(kbase + rw * tok);
-        const auto rv = rsrc(vbase + rw * tok);
+        const Blk bl = block(s, sb);
+        const uint32_t vk = (uint32_t)min(j, bl.rmax) * tok + 16u * q4;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) kr[4 * sb + kk] = bload(rk, voff_k + 64u * kk, 0);
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          dma16(rv, dst + (16 * sb + 4 * i4) * kRowBytes, (i4 & 1) ? voffv1 : voffv0,
-                4 * i4 * tok);
+        for (int kk = 0; kk < 4; ++kk) kr[4 * sb + kk] = bload<kStream>(bl.rk, vk + 64u * kk, 0);
       }
     } else {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        const int tk = min(k0 + 16 * sb + j, ke - 1);      // clamp: finite, never read past
+        const int tk = min(kb + s * kDecodeStep + 16 * sb + j, ke - 1);
         const char* pk = kbase + addr.row(tk) * tok + 16 * q4;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) kr[4 * sb + kk] = gload(pk + 64 * kk);
       }
+    }
+  };
+  auto load_v = [&](int s, char* dst) {
+    if (KVM != KV_PAGED_NARROW) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const Blk bl = block(s, sb);
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int r = 4 * i4 + dq;
+          const uint32_t vv = (uint32_t)min(r, bl.rmax) * tok + 16u * (dc ^ vswz(r));
+          dma16<kStream>(bl.rv, dst + (16 * sb + 4 * i4) * kRowBytes, vv, 0);
+        }
+      }
+    } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = 4 * i + dq;
-        const int tv = min(k0 + r, ke - 1);
+        const int tv = min(kb + s * kDecodeStep + r, ke - 1);
         *(u32x4*)(dst + 4 * i * kRowBytes + 16 * lane) =
             gload(vbase + addr.row(tv) * tok + 16 * (dc ^ vswz(r)));
       }
@@ -467,7 +537,11 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
   const int vrow0 = 4 * q4 + (j >> 2);
   const int vsw = vswz(vrow0);
 
-  auto compute_step = [&](int s, const u32x4 (&kr)[8], bool more) {
+  // Step s: S(s) from K(s) registers and softmax; V(s) read from LDS; then
+  // the DMA of V(s+1) into the other buffer is issued and PV runs.  With
+  // `more`, K(s+1) (8 loads) was requested after the DMA of V(s), so V(s) has
+  // landed once at most 8 loads are outstanding.
+  auto step = [&](int s, const u32x4 (&kr)[8], const char* vsrc, char* vnext, bool more) {
     const int k0 = kb + s * kDecodeStep;
     f32x4 s0 = {}, s1 = {};
 #pragma unroll
@@ -512,30 +586,45 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
     // P^T operand: e = 0..3 -> key 4*q4 + e, e = 4..7 -> key 16 + 4*q4 + e - 4
     const u32x4 pb = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
                       pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
-    // this step's V must have landed: only the next step's 16 loads may be pending
-    if (more) wait_vmem<16>();
+    const char* vt = vsrc + vrow0 * kRowBytes + 8 * (j & 1);
+    if (more) wait_vmem<8>();
     else wait_vmem<0>();
     lds_fence();
-    const char* vt = vbuf(s) + vrow0 * kRowBytes + 8 * (j & 1);
+    u32x4 af[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const char* cp = vt + 16 * ((2 * db + ((j & 3) >> 1)) ^ vsw);
       const u32x2 lo = tr_read(cp);
       const u32x2 hi = tr_read(cp + 16 * kRowBytes);
-      const u32x4 af = {lo[0], lo[1], hi[0], hi[1]};
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(af), as_bf(pb), o[db], 0, 0, 0);
+      af[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
     lds_fence();
+    if (more) load_v(s + 1, vnext);
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(af[db]), as_bf(pb), o[db], 0, 0, 0);
   };
 
+  // The steady-state loop covers step pairs that both have a successor, so
+  // every pass issues the same loads; the last one or two steps follow it.
   u32x4 ka[8], kn[8];
-  if (nsteps > 0) load_step(0, ka);
-  for (int s = 0; s < nsteps; s += 2) {
-    if (s + 1 < nsteps) load_step(s + 1, kn);
-    compute_step(s, ka, s + 1 < nsteps);
-    if (s + 1 >= nsteps) break;
-    if (s + 2 < nsteps) load_step(s + 2, ka);
-    compute_step(s + 1, kn, s + 2 < nsteps);
+  if (nsteps > 0) {
+    load_k(0, ka);
+    load_v(0, vb0);
+    int s = 0;
+    for (; s + 2 < nsteps; s += 2) {
+      load_k(s + 1, kn);
+      step(s, ka, vb0, vb1, true);
+      load_k(s + 2, ka);
+      step(s + 1, kn, vb1, vb0, true);
+    }
+    if (s + 1 < nsteps) {
+      load_k(s + 1, kn);
+      step(s, ka, vb0, vb1, true);
+      step(s + 1, kn, vb1, vb0, false);
+    } else {
+      step(s, ka, vb0, vb1, false);
+    }
   }
 
   // epilogue: query j is spread over lanes j, j+16, j+32, j+48
@@ -617,10 +706,24 @@ __device__ __forceinline__ void finish_launch(const KernelArgs& a, bool reset_cu
 // ---------------------------------------------------------------------------
 // Kernels
 // ---------------------------------------------------------------------------
+// The four LDS objects of a workgroup (see the LDS geometry note).  The
+// scheduling words live in the first bytes of object 0 before any tile data
+// and after all of it.
+#define POD_LDS_OBJECTS                                  \
+  __shared__ __align__(16) char ldsx[2 * kTileBytes];    \
+  __shared__ __align__(16) char ldsy[2 * kTileBytes];    \
+  int* const s_info = reinterpret_cast<int*>(ldsx);
+
+// prefill tiles: K0, K1, V0, V1
+#define POD_PREFILL_BUFFERS ldsx, ldsy, ldsy + kTileBytes, ldsx + kTileBytes
+// decode wave w: step buffers of parity 0 / 1
+#define POD_DECODE_BUFFERS(w)                                  \
+  char* const db0 = ldsx + (w) * kDecStepBytes;               \
+  char* const db1 = ldsy + (w) * kDecStepBytes;
+
 template <int KVM>
 __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
-  extern __shared__ __align__(16) char lds[];
-  __shared__ int s_info[4];
+  POD_LDS_OBJECTS
   if (threadIdx.x == 0) {
     const int slot = cu_slot_id();
     const int xcc = slot >> 8;
@@ -675,21 +778,22 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
     }
   }
   __syncthreads();
-  const int role = s_info[0], unit = s_info[1];
+  const int role = s_info[0], unit = s_info[1], slot = s_info[2];
+  __syncthreads();   // every wave holds the words before tile data overwrites them
   if (unit >= 0) {
     if (role == 0) {
-      prefill_tile<KVM>(a, (cptr)a.p_items + rfl(unit) * P_FIELDS, lds);
+      prefill_tile<KVM>(a, (cptr)a.p_items + rfl(unit) * P_FIELDS, POD_PREFILL_BUFFERS);
     } else {
-      const int wave = threadIdx.x >> 6;
+      const int wave = rfl(threadIdx.x >> 6);
       const int d = unit * kWavesPerWG + wave;
-      if (d < a.n_d)
-        decode_unit<KVM>(a, (cptr)a.d_items + rfl(d) * D_FIELDS, lds + rfl(wave) * kDecWaveBytes);
+      POD_DECODE_BUFFERS(wave)
+      if (d < a.n_d) decode_unit<KVM>(a, (cptr)a.d_items + d * D_FIELDS, db0, db1);
     }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     if (a.sched_mode == POD_SCHED_LIVE)
-      atomicSub(&a.cu_counters[s_info[2]], role == 0 ? 1 : (1 << 16));
+      atomicSub(&a.cu_counters[slot], role == 0 ? 1 : (1 << 16));
     if (a.trace) a.trace[blockIdx.x].t_end = __builtin_amdgcn_s_memrealtime();
   }
   finish_launch(a, a.sched_mode == POD_SCHED_TICKET, &s_info[3]);
@@ -697,22 +801,24 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
 
 template <int KVM>
 __global__ __launch_bounds__(256, 2) void pod_prefill_kernel(KernelArgs a) {
-  extern __shared__ __align__(16) char lds[];
-  __shared__ int s_info[2];
+  POD_LDS_OBJECTS
   if (threadIdx.x == 0) s_info[0] = claim_prefill(a, cu_slot_id() >> 8);
   __syncthreads();
   const int unit = s_info[0];
-  if (unit >= 0) prefill_tile<KVM>(a, (cptr)a.p_items + rfl(unit) * P_FIELDS, lds);
+  __syncthreads();
+  if (unit >= 0)
+    prefill_tile<KVM>(a, (cptr)a.p_items + rfl(unit) * P_FIELDS, POD_PREFILL_BUFFERS);
   finish_launch(a, false, &s_info[1]);
 }
 
 template <int KVM>
 __global__ __launch_bounds__(256, 2) void pod_decode_kernel(KernelArgs a) {
-  extern __shared__ __align__(16) char lds[];
-  const int wave = threadIdx.x >> 6;
+  POD_LDS_OBJECTS
+  (void)s_info;
+  const int wave = rfl(threadIdx.x >> 6);
   const int d = blockIdx.x * kWavesPerWG + wave;
-  if (d < a.n_d)
-    decode_unit<KVM>(a, (cptr)a.d_items + rfl(d) * D_FIELDS, lds + rfl(wave) * kDecWaveBytes);
+  POD_DECODE_BUFFERS(wave)
+  if (d < a.n_d) decode_unit<KVM>(a, (cptr)a.d_items + d * D_FIELDS, db0, db1);
 }
 
 __global__ __launch_bounds__(256) void pod_merge_kernel(KernelArgs a) {
@@ -766,44 +872,16 @@ __global__ void pod_probe_kernel(int32_t* out) {
   }                                                                                      \
   return hipGetLastError();
 
-static hipError_t g_lds_attr_err = hipSuccess;
-
-static void set_lds_attrs_once() {
-  const void* fused[3] = {(const void*)pod_fused_kernel<KV_CONTIG>,
-                          (const void*)pod_fused_kernel<KV_PAGED_WIDE>,
-                          (const void*)pod_fused_kernel<KV_PAGED_NARROW>};
-  const void* pre[3] = {(const void*)pod_prefill_kernel<KV_CONTIG>,
-                        (const void*)pod_prefill_kernel<KV_PAGED_WIDE>,
-                        (const void*)pod_prefill_kernel<KV_PAGED_NARROW>};
-  for (int i = 0; i < 3; ++i) {
-    hipError_t e = hipFuncSetAttribute(fused[i], hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       kFusedLdsBytes);
-    if (e != hipSuccess && g_lds_attr_err == hipSuccess) g_lds_attr_err = e;
-    e = hipFuncSetAttribute(pre[i], hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kPrefillLdsBytes);
-    if (e != hipSuccess && g_lds_attr_err == hipSuccess) g_lds_attr_err = e;
-  }
-}
-
-// Dynamic LDS above 64 KiB must be enabled per kernel before its first launch.
-static hipError_t set_lds_attrs() {
-  static std::once_flag once;
-  std::call_once(once, set_lds_attrs_once);
-  return g_lds_attr_err;
-}
-
 hipError_t launch_fused(const KernelArgs& a, int kv_mode, int grid, hipStream_t s) {
-  if (hipError_t e = set_lds_attrs(); e != hipSuccess) return e;
-  POD_DISPATCH(pod_fused_kernel, kFusedLdsBytes)
+  POD_DISPATCH(pod_fused_kernel, 0)
 }
 
 hipError_t launch_prefill(const KernelArgs& a, int kv_mode, int grid, hipStream_t s) {
-  if (hipError_t e = set_lds_attrs(); e != hipSuccess) return e;
-  POD_DISPATCH(pod_prefill_kernel, kPrefillLdsBytes)
+  POD_DISPATCH(pod_prefill_kernel, 0)
 }
 
 hipError_t launch_decode(const KernelArgs& a, int kv_mode, int grid, hipStream_t s) {
-  POD_DISPATCH(pod_decode_kernel, kDecodeLdsBytes)
+  POD_DISPATCH(pod_decode_kernel, 0)
 }
 
 hipError_t launch_merge(const KernelArgs& a, int grid, hipStream_t s) {
