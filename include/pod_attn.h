@@ -64,19 +64,19 @@ typedef enum { POD_KV_CONTIGUOUS = 0, POD_KV_PAGED = 1 } pod_kv_layout_t;
 
 /* Scheduler modes of the fused kernel's per-CU counter. */
 typedef enum {
-  /* The counter holds the live (prefill, decode) workgroup counts of the CU;
-   * an arriving workgroup takes the role that is below its target share. */
+  /* The counter holds the (prefill, decode) counts of the CU's workgroups;
+   * a starting workgroup takes the role that is below its target share. */
   POD_SCHED_LIVE = 0,
   /* The counter is a ticket: role = pattern[ticket % wgs_per_cu], the
    * prefill slots first ([POD] "Self-assign roles per SM in software"). */
   POD_SCHED_TICKET = 1,
-  /* No role steering: workgroup b takes prefill units while they last, then
-   * decode units (a fused launch without co-location control). */
+  /* No role steering: every workgroup takes prefill units while they last,
+   * then decode units (a fused launch without co-location control). */
   POD_SCHED_ORDERED = 2
 } pod_sched_mode_t;
 
 /* tuning flags */
-#define POD_FLAG_TRACE 0x1u   /* fused run records one pod_trace_record_t per WG */
+#define POD_FLAG_TRACE 0x1u   /* fused run records one pod_trace_record_t per unit */
 
 typedef struct pod_attn_plan_s* pod_attn_plan_t;   /* opaque, library-owned */
 
@@ -125,13 +125,14 @@ typedef struct {
   uint64_t workspace_bytes;
 } pod_attn_plan_info_t;
 
-/* One fused-kernel workgroup (POD_FLAG_TRACE). */
+/* One unit of a fused run (POD_FLAG_TRACE): records 0 .. prefill_items-1
+ * are the prefill items, then one per decode item. */
 typedef struct {
-  int32_t block;       /* blockIdx.x */
+  int32_t block;       /* blockIdx.x of the workgroup that ran it */
   int32_t cu_slot;     /* (xcc << 8) | (se << 5) | (sh << 4) | cu */
   int32_t role;        /* 0 prefill, 1 decode */
-  int32_t unit;        /* prefill item or decode group index */
-  uint64_t t_start;    /* s_memrealtime (100 MHz) at claim */
+  int32_t unit;        /* prefill item or decode item index */
+  uint64_t t_start;    /* s_memrealtime (100 MHz) when the unit started */
   uint64_t t_end;      /* s_memrealtime after the unit */
 } pod_trace_record_t;
 
@@ -198,8 +199,9 @@ pod_status_t pod_attn_plan_host(const pod_attn_params_t* params,
                                 const pod_device_desc_t* device,
                                 pod_attn_plan_t* out_plan);
 
-/* Fused run: one kernel for all prefill tiles and decode splits, then the
- * merge kernel if any split exists.  Asynchronous on `stream`.
+/* Fused run: one persistent kernel (two workgroups per CU) for all prefill
+ * tiles and decode splits, then the merge kernel if any split exists.
+ * Asynchronous on `stream`.
  * Errors: POD_ERR_INVALID_ARGUMENT (NULL plan/tensors, a required pointer
  * NULL or not 16-byte aligned, plan without workspace), POD_ERR_HIP. */
 pod_status_t pod_attn_run(pod_attn_plan_t plan, const pod_attn_tensors_t* t,
@@ -218,9 +220,9 @@ pod_status_t pod_attn_plan_info(pod_attn_plan_t plan, pod_attn_plan_info_t* out)
 /* Copies one of the plan's host work lists into dst (host int32, capacity n
  * elements); *count receives the element count (dst may be NULL to query).
  * which: 0 fused prefill items (8 int32 each), 1 fused decode items (8 each),
- * 2 fused merge tasks (4 each), 3/4/5 the sequential lists, 6 the prefill
- * pool offsets (num_xcds + 1).  Item fields are documented in plan.h of the
- * sources.  Errors: POD_ERR_INVALID_ARGUMENT. */
+ * 2 fused merge tasks (4 each), 3/4/5 the sequential lists, 6/7 the fused /
+ * sequential prefill pool offsets (num_xcds + 1 each).  Item fields are
+ * documented in plan.h of the sources.  Errors: POD_ERR_INVALID_ARGUMENT. */
 pod_status_t pod_attn_plan_export(pod_attn_plan_t plan, int32_t which,
                                   int32_t* dst, size_t n, size_t* count);
 

@@ -19,9 +19,13 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-# Packed fp32 instructions are disabled (hipcc forms them on its own).
+# Packed fp32 instructions are disabled (hipcc forms them on its own).  The
+# atomic optimizer is off: it turns a one-lane claim into a wave-aggregated
+# atomic whose result is read at once, which would stall every prefetched
+# work claim for the atomic's full latency.
 HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
              "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
              f"-I{ROCM}/include"]

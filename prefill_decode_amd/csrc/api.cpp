@@ -88,17 +88,16 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   const int64_t fused_p_slots = sum_qo <= 1536 ? p_slots_coloc : slots;
   const int64_t fused_d_waves =
       std::max<int64_t>(kWavesPerWG, (int64_t)dev.num_cus * (4 * c.wgs_per_cu - c.prefill_quarters));
-  build_lists(pl->batch, dev, fused_p_slots, fused_d_waves, t.prefill_kv_splits,
-              t.decode_kv_splits, &pl->fused);
+  build_lists(pl->batch, dev, fused_p_slots, fused_d_waves, kFusedDecodeUnitsPerWave,
+              t.prefill_kv_splits, t.decode_kv_splits, &pl->fused);
   // Sequential plan: each kernel has the whole GPU.
   pl->seq_is_fused = t.match_sequential == 1;
   if (!pl->seq_is_fused)
-    build_lists(pl->batch, dev, slots, slots * kWavesPerWG, t.prefill_kv_splits,
-                t.decode_kv_splits, &pl->seq);
+    build_lists(pl->batch, dev, slots, slots * kWavesPerWG, kSeqDecodeUnitsPerWave,
+                t.prefill_kv_splits, t.decode_kv_splits, &pl->seq);
   const WorkLists& sq = pl->seq_is_fused ? pl->fused : pl->seq;
   pl->n_partials = std::max(pl->fused.n_partials, sq.n_partials);
-  const int32_t grid_fused = pl->fused.n_p() + pl->fused.n_groups();
-  pl->trace_records = (t.flags & POD_FLAG_TRACE) ? grid_fused : 0;
+  pl->trace_records = (t.flags & POD_FLAG_TRACE) ? pl->fused.n_p() + pl->fused.n_d() : 0;
 
   // workspace layout
   size_t off = 0;
@@ -212,13 +211,14 @@ KernelArgs make_args(const pod_attn_plan_s* pl, const pod_attn_tensors_t* t, con
   a.m_tasks = (const int32_t*)(pl->ws + dl.m_tasks);
   int32_t* ctr = (int32_t*)(pl->ws + pl->off_counters);
   a.counters = ctr + counter_block;
-  a.cu_counters = ctr;
+  a.cu_counters = ctr + kCuCounterOff;
   a.trace = nullptr;
   a.n_p = w.n_p();
   a.n_d = w.n_d();
   a.n_groups = w.n_groups();
   a.n_m = w.n_m();
   a.num_pools = (int32_t)w.pool_off.size() - 1;
+  a.n_dq = a.num_pools;
   for (int i = 0; i <= a.num_pools && i <= kMaxPools; ++i) a.pool_off[i] = w.pool_off[i];
   a.hq = p.num_qo_heads;
   a.hkv = p.num_kv_heads;
@@ -338,7 +338,9 @@ pod_status_t pod_attn_run(pod_attn_plan_t pl, const pod_attn_tensors_t* t, hipSt
   const WorkLists& w = pl->fused;
   KernelArgs a = make_args(pl, t, w, pl->dl_fused, kFusedBlock);
   if (pl->trace_records) a.trace = (pod_trace_record_t*)(pl->ws + pl->off_trace);
-  const int grid = w.n_p() + w.n_groups();
+  // persistent: wgs_per_cu workgroups per CU, fewer when there are fewer units
+  const int64_t slots = (int64_t)pl->dev.num_cus * pl->choice.wgs_per_cu;
+  const int grid = (int)std::min<int64_t>(slots, (int64_t)w.n_p() + w.n_groups());
   if (grid > 0) {
     hipError_t e = launch_fused(a, kv_mode_of(pl), grid, stream);
     if (e != hipSuccess) return hip_err(e, "fused kernel launch");

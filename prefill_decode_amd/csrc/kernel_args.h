@@ -10,14 +10,22 @@ namespace pod {
 
 constexpr int kMaxPools = 16;
 
-// Counter block layout (int32 offsets inside a plan's counter region).
+// Counter layout.  A run's claim and completion counters are device-scope
+// atomics, which the MI355X serialises per address (about 11 ns each, a few
+// hundred ns of latency); each hot counter therefore gets its own 4 KiB so
+// that counters of different XCDs proceed in parallel.
+constexpr int kCtrStride = 1024;           // ints between two hot counters
+constexpr int CS_POOL = 0;                 // +pool: claims from prefill pool (< kMaxPools)
+constexpr int CS_DQ = 16;                  // +queue: claims from decode queue (< kMaxPools)
+constexpr int CS_DONE = 32;                // +g (8 groups by blockIdx % 8): finished WGs
+constexpr int CS_DONE_ALL = 40;            // groups whose WGs all finished
+constexpr int kCtrSlots = 41;
+constexpr int kCtrBlockInts = kCtrSlots * kCtrStride;
+constexpr int kFusedBlock = 0;             // fused kernel's counter block
+constexpr int kSeqBlock = kCtrBlockInts;   // sequential prefill kernel's block
+constexpr int kCuCounterOff = 2 * kCtrBlockInts;
 constexpr int kCuCounters = 2048;          // per-CU role counters (fused kernel)
-constexpr int kFusedBlock = 2048;          // fused: pools, decode, done
-constexpr int kSeqBlock = 2048 + 32;       // sequential prefill: pools, done
-constexpr int kCounterInts = 4096;
-constexpr int C_POOL = 0;                  // +pool: claims taken from prefill pool
-constexpr int C_DEC = 16;                  // claims taken from the decode groups
-constexpr int C_DONE = 17;                 // workgroups finished
+constexpr int kCounterInts = kCuCounterOff + kCuCounters;
 
 // KV addressing modes (kernel template parameter).
 enum KvMode : int { KV_CONTIG = 0, KV_PAGED_WIDE = 1, KV_PAGED_NARROW = 2 };
@@ -41,6 +49,7 @@ struct KernelArgs {
   const int32_t* m_tasks;
   int32_t* counters;      // the launch's counter block (fused or sequential)
   int32_t* cu_counters;   // per-CU counters (fused)
+  int32_t n_dq;           // decode queues (one per XCD): queue q holds units q, q+n_dq, ..
   pod_trace_record_t* trace;
   int32_t n_p, n_d, n_groups, n_m;
   int32_t num_pools;

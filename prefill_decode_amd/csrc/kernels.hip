@@ -661,58 +661,95 @@ __device__ __forceinline__ int cu_slot_id() {
   return (int)(((xcc & 7) << 8) | (se << 5) | (sh << 4) | cu);
 }
 
+__device__ __forceinline__ int* hot(const KernelArgs& a, int i) {
+  return a.counters + i * kCtrStride;
+}
+__device__ __forceinline__ int peek(int* c) {
+  return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Prefill claim (one thread): the pool of this XCD first, then the others.
 __device__ __forceinline__ int claim_prefill(const KernelArgs& a, int xcc) {
   for (int i = 0; i < a.num_pools; ++i) {
     const int p = (xcc + i) % a.num_pools;
     const int n = a.pool_off[p + 1] - a.pool_off[p];
     if (n <= 0) continue;
-    if (__hip_atomic_load(&a.counters[C_POOL + p], __ATOMIC_RELAXED,
-                          __HIP_MEMORY_SCOPE_AGENT) >= n)
-      continue;
-    const int c = atomicAdd(&a.counters[C_POOL + p], 1);
-    if (c < n) return a.pool_off[p] + c;
+    int* c = hot(a, CS_POOL + p);
+    if (peek(c) >= n) continue;
+    const int k = atomicAdd(c, 1);
+    if (k < n) return a.pool_off[p] + k;
   }
   return -1;
 }
 
-__device__ __forceinline__ int claim_decode(const KernelArgs& a) {
-  if (a.n_groups <= 0) return -1;
-  if (__hip_atomic_load(&a.counters[C_DEC], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-      a.n_groups)
-    return -1;
-  const int c = atomicAdd(&a.counters[C_DEC], 1);
-  return c < a.n_groups ? c : -1;
+// Decode claim (one wavefront, result uniform): units are ordered longest
+// first and dealt round-robin to n_dq queues (queue q: units q, q + n_dq, ..),
+// so every queue is balanced and longest first too.  Queue q0 (this XCD's)
+// first, then the others.
+__device__ __forceinline__ int claim_decode_from(const KernelArgs& a, int q0) {
+  const int nq = a.n_dq;
+  for (int i = 0; i < nq; ++i) {
+    const int q = (q0 + i) % nq;
+    int u = a.n_d;
+    if (__lane_id() == 0) {
+      int* c = hot(a, CS_DQ + q);
+      if (q + nq * peek(c) < a.n_d) u = q + nq * atomicAdd(c, 1);
+    }
+    u = rfl(u);
+    if (u < a.n_d) return u;
+  }
+  return -1;
 }
 
-// Last workgroup of a launch resets the launch's claim counters (and, for the
-// ticket scheduler, the per-CU tickets) so the next run starts from zero.
+// Last workgroup of a launch resets the launch's counters (and the per-CU
+// role counters), so the next run starts from zero.  Completion is counted in
+// two levels (8 groups by blockIdx, then the groups) to keep the per-address
+// atomic traffic low.  Every claim a workgroup made returned before it counts
+// itself done (each returned value was used), and each level's atomic is
+// issued after the previous one returned, so no memory fence is needed.
 __device__ __forceinline__ void finish_launch(const KernelArgs& a, bool reset_cu,
                                               int* s_last) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
-    const int d = atomicAdd(&a.counters[C_DONE], 1);
-    *s_last = (d == (int)gridDim.x - 1);
+    const int g = (int)blockIdx.x & 7;
+    const int n_g = ((int)gridDim.x - g + 7) >> 3;
+    int last = 0;
+    if (atomicAdd(hot(a, CS_DONE + g), 1) == n_g - 1) {
+      const int groups = min(8, (int)gridDim.x);
+      last = atomicAdd(hot(a, CS_DONE_ALL), 1) == groups - 1;
+    }
+    *s_last = last;
   }
   __syncthreads();
   if (*s_last) {
-    __threadfence();
-    if (threadIdx.x < 18) a.counters[threadIdx.x] = 0;
+    for (int i = threadIdx.x; i < kCtrSlots; i += blockDim.x)
+      __hip_atomic_store(hot(a, i), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (reset_cu)
-      for (int i = threadIdx.x; i < kCuCounters; i += blockDim.x) a.cu_counters[i] = 0;
+      for (int i = threadIdx.x; i < kCuCounters; i += blockDim.x)
+        __hip_atomic_store(&a.cu_counters[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+__device__ __forceinline__ void trace_unit(const KernelArgs& a, int rec, int role, int unit,
+                                           int slot, uint64_t t0) {
+  pod_trace_record_t* r = a.trace + rec;
+  r->block = (int)blockIdx.x;
+  r->cu_slot = slot;
+  r->role = role;
+  r->unit = unit;
+  r->t_start = t0;
+  r->t_end = __builtin_amdgcn_s_memrealtime();
 }
 
 // ---------------------------------------------------------------------------
 // Kernels
 // ---------------------------------------------------------------------------
-// The four LDS objects of a workgroup (see the LDS geometry note).  The
-// scheduling words live in the first bytes of object 0 before any tile data
-// and after all of it.
+// The two LDS tile objects of a workgroup (see the LDS geometry note) and a
+// few scheduling words.
 #define POD_LDS_OBJECTS                                  \
   __shared__ __align__(16) char ldsx[2 * kTileBytes];    \
   __shared__ __align__(16) char ldsy[2 * kTileBytes];    \
-  int* const s_info = reinterpret_cast<int*>(ldsx);
+  __shared__ int s_info[8];
 
 // prefill tiles: K0, K1, V0, V1
 #define POD_PREFILL_BUFFERS ldsx, ldsy, ldsy + kTileBytes, ldsx + kTileBytes
@@ -721,13 +758,20 @@ __device__ __forceinline__ void finish_launch(const KernelArgs& a, bool reset_cu
   char* const db0 = ldsx + (w) * kDecStepBytes;               \
   char* const db1 = ldsy + (w) * kDecStepBytes;
 
+// Fused kernel: one persistent launch of wgs_per_cu workgroups per CU.  A
+// workgroup reads which CU it landed on, takes its first role from that CU's
+// counter (prefill for its share of the CU's slots), and works through the
+// queue of that role: prefill tiles one workgroup at a time, decode units one
+// wavefront at a time (each wave claims its own next unit, no workgroup
+// barrier between units).  When its queue runs dry it moves to the other
+// queue, so no slot idles while work is left.
 template <int KVM>
 __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
   POD_LDS_OBJECTS
-  if (threadIdx.x == 0) {
+  const int tid = threadIdx.x;
+  const int wave = rfl(tid >> 6), lane = tid & 63;
+  if (tid == 0) {
     const int slot = cu_slot_id();
-    const int xcc = slot >> 8;
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     int role;   // 0 prefill, 1 decode
     int* cell = &a.cu_counters[slot];
     const int tp = (a.prefill_quarters + (slot & 3)) >> 2;   // prefill target of this CU
@@ -736,7 +780,7 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
       int old = __hip_atomic_load(cell, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       while (true) {
         const int lp = old & 0xFFFF, ld = old >> 16;
-        // take the role whose live count is furthest below its target share
+        // take the role whose count is furthest below its target share
         role = (td <= 0) ? 0 : (tp <= 0) ? 1 : ((lp + 1) * td <= (ld + 1) * tp ? 0 : 1);
         const int nw = old + (role == 0 ? 1 : (1 << 16));
         const int got = atomicCAS(cell, old, nw);
@@ -749,54 +793,48 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
     } else {
       role = 0;
     }
-    int unit;
-    if (role == 0) {
-      unit = claim_prefill(a, xcc);
-      if (unit < 0) {
-        role = 1;
-        unit = claim_decode(a);
-        if (a.sched_mode == POD_SCHED_LIVE) atomicAdd(cell, (1 << 16) - 1);
-      }
-    } else {
-      unit = claim_decode(a);
-      if (unit < 0) {
-        role = 0;
-        unit = claim_prefill(a, xcc);
-        if (a.sched_mode == POD_SCHED_LIVE) atomicAdd(cell, 1 - (1 << 16));
-      }
-    }
     s_info[0] = role;
-    s_info[1] = unit;
-    s_info[2] = slot;
-    if (a.trace) {
-      pod_trace_record_t* r = a.trace + blockIdx.x;
-      r->block = blockIdx.x;
-      r->cu_slot = slot;
-      r->role = role;
-      r->unit = unit;
-      r->t_start = t0;
-    }
+    s_info[1] = slot;
   }
   __syncthreads();
-  const int role = s_info[0], unit = s_info[1], slot = s_info[2];
-  __syncthreads();   // every wave holds the words before tile data overwrites them
-  if (unit >= 0) {
-    if (role == 0) {
-      prefill_tile<KVM>(a, (cptr)a.p_items + rfl(unit) * P_FIELDS, POD_PREFILL_BUFFERS);
-    } else {
-      const int wave = rfl(threadIdx.x >> 6);
-      const int d = unit * kWavesPerWG + wave;
-      POD_DECODE_BUFFERS(wave)
-      if (d < a.n_d) decode_unit<KVM>(a, (cptr)a.d_items + d * D_FIELDS, db0, db1);
+  const int role0 = s_info[0], slot = s_info[1];
+  const int xcc = slot >> 8;
+  // ---- prefill tiles until the pools are empty.  A unit is claimed only
+  // when the claimant is free (greedy list scheduling: the next unit goes to
+  // the first worker to finish, which a claim made ahead of time would not
+  // honour); a claim costs well under 1% of a unit. ----
+  auto prefill_phase = [&]() {
+    while (true) {
+      __syncthreads();   // the previous unit / phase is done with LDS and s_info
+      if (tid == 0) s_info[2] = claim_prefill(a, xcc);
+      __syncthreads();
+      const int u = rfl(s_info[2]);
+      if (u < 0) break;
+      const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
+      prefill_tile<KVM>(a, (cptr)a.p_items + u * P_FIELDS, POD_PREFILL_BUFFERS);
+      if (a.trace && tid == 0) trace_unit(a, u, 0, u, slot, t0);
     }
+  };
+  // ---- decode units until the queues are empty, one per wavefront ----
+  auto decode_phase = [&]() {
+    __syncthreads();   // the previous phase is done with LDS
+    POD_DECODE_BUFFERS(wave)
+    const int q0 = xcc % a.n_dq;
+    int u;
+    while ((u = claim_decode_from(a, q0)) >= 0) {
+      const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
+      decode_unit<KVM>(a, (cptr)a.d_items + u * D_FIELDS, db0, db1);
+      if (a.trace && lane == 0) trace_unit(a, a.n_p + u, 1, u, slot, t0);
+    }
+  };
+  if (role0 == 0) {
+    prefill_phase();
+    decode_phase();
+  } else {
+    decode_phase();
+    prefill_phase();
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    if (a.sched_mode == POD_SCHED_LIVE)
-      atomicSub(&a.cu_counters[slot], role == 0 ? 1 : (1 << 16));
-    if (a.trace) a.trace[blockIdx.x].t_end = __builtin_amdgcn_s_memrealtime();
-  }
-  finish_launch(a, a.sched_mode == POD_SCHED_TICKET, &s_info[3]);
+  finish_launch(a, true, &s_info[4]);
 }
 
 template <int KVM>

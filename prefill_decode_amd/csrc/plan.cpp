@@ -116,8 +116,8 @@ int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu) {
 }
 
 void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_slots,
-                 int64_t decode_wave_slots, int32_t force_p_splits, int32_t force_d_splits,
-                 WorkLists* out) {
+                 int64_t decode_wave_slots, int32_t d_units_per_slot, int32_t force_p_splits,
+                 int32_t force_d_splits, WorkLists* out) {
   const auto& p = b.params;
   const int32_t hq = p.num_qo_heads, hkv = p.num_kv_heads, g = hq / hkv;
   const int32_t np = (int32_t)b.qo.size(), nd = (int32_t)b.dkv.size();
@@ -211,7 +211,8 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
   for (int32_t k : b.dkv) total_keys += double(k) * hkv * qchunks;
   int64_t chunk = kMinDecodeChunk;
   if (decode_wave_slots > 0 && total_keys > 0) {
-    const int64_t c = (int64_t)std::ceil(total_keys / double(2 * decode_wave_slots));
+    const int64_t c =
+        (int64_t)std::ceil(total_keys / double(std::max(1, d_units_per_slot) * decode_wave_slots));
     chunk = std::max<int64_t>(chunk, ceil_div(c, kDecodeStep) * kDecodeStep);
   }
   struct DI { std::array<int32_t, D_FIELDS> f; int32_t work; };
@@ -252,7 +253,8 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
         }
       }
   }
-  // longest first, so that the four waves of a decode workgroup get similar work
+  // longest first: claimed in this order, the last units to start are the
+  // shortest (and the four waves of a sequential decode workgroup get similar work)
   std::stable_sort(ditems.begin(), ditems.end(),
                    [](const DI& a, const DI& c) { return a.work > c.work; });
   for (auto& it : ditems) w.d_items.insert(w.d_items.end(), it.f.begin(), it.f.end());

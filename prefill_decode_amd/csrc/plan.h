@@ -28,6 +28,8 @@ constexpr int kMaxXcds = 16;
 constexpr int kMaxPrefillSplits = 16;
 constexpr int kMaxDecodeSplits = 64;
 constexpr int kMinDecodeChunk = 512;   // keys per decode split, lower bound
+constexpr int kFusedDecodeUnitsPerWave = 4;   // fused: units claimed per wave, dynamic
+constexpr int kSeqDecodeUnitsPerWave = 2;     // sequential: one wave per unit, grid order
 
 // Prefill work item (8 int32).
 enum PItem : int {
@@ -99,9 +101,11 @@ pod_status_t validate(const pod_attn_params_t* p, int32_t np, const int32_t* qo,
 int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu);
 
 // Builds one set of work lists.  `prefill_slots` / `decode_wave_slots` are the
-// concurrent prefill workgroups / decode wavefronts the splits should fill.
+// concurrent prefill workgroups / decode wavefronts the splits should fill;
+// decode requests are split until there are about `d_units_per_slot` units
+// per decode wavefront (chunks of at least kMinDecodeChunk keys).
 void build_lists(const Batch& b, const pod_device_desc_t& dev,
-                 int64_t prefill_slots, int64_t decode_wave_slots,
+                 int64_t prefill_slots, int64_t decode_wave_slots, int32_t d_units_per_slot,
                  int32_t force_p_splits, int32_t force_d_splits, WorkLists* out);
 
 }  // namespace pod

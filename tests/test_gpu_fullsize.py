@@ -59,10 +59,13 @@ def test_colocation_trace():
     run_path(runner, "fused")
     info = runner.plan.info()
     tr = runner.plan.read_trace()
-    assert len(tr) == info["prefill_items"] + info["decode_groups"]
+    n_p, n_d = info["prefill_items"], info["decode_items"]
+    assert len(tr) == n_p + n_d
     role, unit, slot = tr[:, 2], tr[:, 3], tr[:, 1]
-    assert sorted(unit[role == 0].tolist()) == list(range(info["prefill_items"]))
-    assert sorted(unit[role == 1].tolist()) == list(range(info["decode_groups"]))
+    # every unit ran exactly once, in the record of its index
+    assert np.array_equal(role, np.r_[np.zeros(n_p), np.ones(n_d)].astype(role.dtype))
+    assert np.array_equal(unit, np.r_[np.arange(n_p), np.arange(n_d)].astype(unit.dtype))
+    assert np.all(tr[:, 5] >= tr[:, 4])
     both = 0
     slots = np.unique(slot)
     for s in slots:
