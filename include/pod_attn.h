@@ -207,6 +207,16 @@ pod_status_t pod_attn_plan_host(const pod_attn_params_t* params,
 pod_status_t pod_attn_run(pod_attn_plan_t plan, const pod_attn_tensors_t* t,
                           hipStream_t stream);
 
+/* pod_attn_run that also records two caller-created events on `stream`,
+ * immediately before and after the fused kernel's launch (the merge kernel,
+ * when any, follows `after_fused`), so that the fused kernel alone can be
+ * timed.  Either event may be NULL (not recorded).  The work done is exactly
+ * that of pod_attn_run.  Errors as pod_attn_run, plus POD_ERR_HIP when an
+ * event cannot be recorded. */
+pod_status_t pod_attn_run_events(pod_attn_plan_t plan, const pod_attn_tensors_t* t,
+                                 hipStream_t stream, hipEvent_t before_fused,
+                                 hipEvent_t after_fused);
+
 /* Sequential baseline: prefill kernel, then decode kernel, then merge, on
  * `stream`.  Uses its own work lists (splits sized for a GPU running one
  * part at a time) unless the plan was made with match_sequential = 1.

@@ -25,7 +25,8 @@ SCHED_LIVE, SCHED_TICKET, SCHED_ORDERED = 0, 1, 2
 FLAG_TRACE = 0x1
 
 # every function the header declares
-EXPORTED = ("pod_attn_plan", "pod_attn_plan_host", "pod_attn_run", "pod_attn_sequential_run",
+EXPORTED = ("pod_attn_plan", "pod_attn_plan_host", "pod_attn_run", "pod_attn_run_events",
+            "pod_attn_sequential_run",
             "pod_attn_plan_info", "pod_attn_plan_export", "pod_attn_read_trace",
             "pod_attn_plan_destroy", "pod_attn_last_error", "pod_attn_probe_hwid")
 
@@ -91,6 +92,8 @@ def lib():
                                          i32p, C.POINTER(Tuning), C.POINTER(DeviceDesc),
                                          C.POINTER(C.c_void_p)]
         L.pod_attn_run.argtypes = [C.c_void_p, C.POINTER(Tensors), C.c_void_p]
+        L.pod_attn_run_events.argtypes = [C.c_void_p, C.POINTER(Tensors), C.c_void_p,
+                                          C.c_void_p, C.c_void_p]
         L.pod_attn_sequential_run.argtypes = [C.c_void_p, C.POINTER(Tensors), C.c_void_p]
         L.pod_attn_plan_info.argtypes = [C.c_void_p, C.POINTER(PlanInfo)]
         L.pod_attn_plan_export.argtypes = [C.c_void_p, C.c_int32, i32p, C.c_size_t,
@@ -244,6 +247,17 @@ def run(p: Plan, tensors: Tensors, stream=None):
     _check(lib().pod_attn_run(p.handle, C.byref(tensors), _stream(stream)))
 
 
+def run_events(p: Plan, tensors: Tensors, before_fused, after_fused, stream=None):
+    """`run` recording two torch.cuda.Event objects (timing enabled) on the
+    stream immediately around the fused kernel's launch."""
+    for e in (before_fused, after_fused):
+        if not e.cuda_event:          # torch creates the HIP event on first record
+            e.record()
+    _check(lib().pod_attn_run_events(p.handle, C.byref(tensors), _stream(stream),
+                                     C.c_void_p(before_fused.cuda_event),
+                                     C.c_void_p(after_fused.cuda_event)))
+
+
 def sequential_run(p: Plan, tensors: Tensors, stream=None):
     """Prefill kernel, then decode kernel, then merge (asynchronous)."""
     _check(lib().pod_attn_sequential_run(p.handle, C.byref(tensors), _stream(stream)))
@@ -304,6 +318,9 @@ class BatchRunner:
 
     def run(self, stream=None):
         run(self.plan, self.tensors, stream)
+
+    def run_events(self, before_fused, after_fused, stream=None):
+        run_events(self.plan, self.tensors, before_fused, after_fused, stream)
 
     def sequential_run(self, stream=None):
         sequential_run(self.plan, self.tensors, stream)

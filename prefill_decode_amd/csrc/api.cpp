@@ -332,7 +332,9 @@ pod_status_t pod_attn_plan(const pod_attn_params_t* params, int32_t num_prefill,
   return POD_OK;
 }
 
-pod_status_t pod_attn_run(pod_attn_plan_t pl, const pod_attn_tensors_t* t, hipStream_t stream) {
+pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t,
+                                 hipStream_t stream, hipEvent_t before_fused,
+                                 hipEvent_t after_fused) {
   pod_status_t st = check_tensors(pl, t);
   if (st != POD_OK) return st;
   const WorkLists& w = pl->fused;
@@ -341,15 +343,24 @@ pod_status_t pod_attn_run(pod_attn_plan_t pl, const pod_attn_tensors_t* t, hipSt
   // persistent: wgs_per_cu workgroups per CU, fewer when there are fewer units
   const int64_t slots = (int64_t)pl->dev.num_cus * pl->choice.wgs_per_cu;
   const int grid = (int)std::min<int64_t>(slots, (int64_t)w.n_p() + w.n_groups());
+  hipError_t e;
+  if (before_fused && (e = hipEventRecord(before_fused, stream)) != hipSuccess)
+    return hip_err(e, "hipEventRecord(before_fused)");
   if (grid > 0) {
-    hipError_t e = launch_fused(a, kv_mode_of(pl), grid, stream);
+    e = launch_fused(a, kv_mode_of(pl), grid, stream);
     if (e != hipSuccess) return hip_err(e, "fused kernel launch");
   }
+  if (after_fused && (e = hipEventRecord(after_fused, stream)) != hipSuccess)
+    return hip_err(e, "hipEventRecord(after_fused)");
   if (w.n_m() > 0) {
-    hipError_t e = launch_merge(a, (w.n_m() + kWavesPerWG - 1) / kWavesPerWG, stream);
+    e = launch_merge(a, (w.n_m() + kWavesPerWG - 1) / kWavesPerWG, stream);
     if (e != hipSuccess) return hip_err(e, "merge kernel launch");
   }
   return POD_OK;
+}
+
+pod_status_t pod_attn_run(pod_attn_plan_t pl, const pod_attn_tensors_t* t, hipStream_t stream) {
+  return pod_attn_run_events(pl, t, stream, nullptr, nullptr);
 }
 
 pod_status_t pod_attn_sequential_run(pod_attn_plan_t pl, const pod_attn_tensors_t* t,

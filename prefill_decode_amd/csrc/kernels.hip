@@ -194,7 +194,11 @@ template <int KVM>
 __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char* __restrict__ kt0,
                                              char* __restrict__ kt1, char* __restrict__ vt0,
                                              char* __restrict__ vt1) {
-  const int tid = threadIdx.x, lane = tid & 63;
+  // The thread index passes through an empty asm so that nothing derived
+  // from it is hoisted out of a caller's work loop and kept live across it.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = rfl(tid >> 6);
   const int hl = lane >> 5;            // half of the wave
   const int l32 = lane & 31;
@@ -299,17 +303,30 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
     voff[db] = (uint32_t)(vrow0 * kRowBytes +
                           16 * ((4 * db + 2 * (g16 & 1) + ((j16 & 3) >> 1)) ^ vsw) + 8 * (j16 & 1));
 
-  // the two key blocks' accumulation chains are interleaved so that
-  // consecutive MFMAs are independent
+  // S^T(t) = K(t) Q^T: two key blocks' accumulation chains interleaved so
+  // that consecutive MFMAs are independent; eight K operand reads (four
+  // k-steps) are kept in flight ahead of the MFMAs.
   auto qk = [&](int buf, f32x16 (&s)[2]) {
+    const char* kb = buf ? kt1 : kt0;
+    u32x4 ka[8], kc[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      ka[kk] = *(const u32x4*)(kb + koff[kk]);
+      kc[kk] = *(const u32x4*)(kb + koff[kk] + 32 * kRowBytes);
+    }
     f32x16 a0 = {}, a1 = {};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const char* kp = (buf ? kt1 : kt0) + koff[kk];
-      a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(*(const u32x4*)kp), as_bf(qf[kk]), a0,
-                                                   0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          as_bf(*(const u32x4*)(kp + 32 * kRowBytes)), as_bf(qf[kk]), a1, 0, 0, 0);
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(ka[kk]), as_bf(qf[kk]), a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kc[kk]), as_bf(qf[kk]), a1, 0, 0, 0);
+    }
+    // 8 reads up front, then per k-step: 2 MFMAs, the 2 reads of k-step + 4
+#pragma unroll
+    for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (kk < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     s[0] = a0;
     s[1] = a1;
@@ -317,61 +334,69 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  // four independent accumulation chains (d blocks), interleaved
-  auto pv = [&](int buf, const u32x4 (&pb)[4]) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int r0 = 32 * (kk >> 1) + 16 * (kk & 1);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const char* cp = (buf ? vt1 : vt0) + voff[db];
-        const u32x2 lo = tr_read(cp + r0 * kRowBytes);
-        const u32x2 hi = tr_read(cp + (r0 + 8) * kRowBytes);
-        const u32x4 af = {lo[0], lo[1], hi[0], hi[1]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(af), as_bf(pb[kk]), o[db], 0, 0, 0);
-      }
-    }
-  };
 
+  // Online softmax with a lazy reference max: a row's reference m_run moves
+  // only when the row max exceeds it by more than kLazyLog2, so that P =
+  // exp2(s - m_run) <= 2^kLazyLog2 (exact in fp32, one bf16 rounding as any
+  // P) and the rescale of O -- which would have to wait for the previous
+  // tile's P V product -- is rare.  O / l are normalised by the same m_run at
+  // the end, so the result is the softmax either way.
+  constexpr float kLazyLog2 = 8.0f;
   float m_run = kNegInf, l_run = 0.0f;
-  // softmax of tile t (lane: one query row, 32 keys) -> P^T operands
-  auto softmax = [&](int t, f32x16 (&s)[2], u32x4 (&pb)[4]) {
-    if (t >= t_mask) {
-      const int k0 = kv_begin + t * kPrefillKeys + 4 * hl;
+  auto mask_tile = [&](int t, f32x16 (&s)[2]) {
+    const int k0 = kv_begin + t * kPrefillKeys + 4 * hl;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * sb + 8 * (r >> 2) + (r & 3);
-          if (key >= kv_end || (causal && key > qpos)) s[sb][r] = kNegInf;
-        }
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 32 * sb + 8 * (r >> 2) + (r & 3);
+        if (key >= kv_end || (causal && key > qpos)) s[sb][r] = kNegInf;
+      }
+  };
+  // scale a pending P^T operand (bf16 pairs) by the lane's alpha
+  auto scale_p = [&](u32x4 (&p)[4], float alpha) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = p[kk][e];
+        p[kk][e] = pack_bf16x2(__uint_as_float(w << 16) * alpha,
+                               __uint_as_float(w & 0xFFFF0000u) * alpha);
+      }
+  };
+  // row max of S(t); moves m_run (and rescales O, l and the pending P) when
+  // some row's max has grown past the lazy bound
+  auto update_max = [&](f32x16 (&s)[2], bool pending, u32x4 (&pp)[4]) {
     float mx = kNegInf;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmax_(mx, s[sb][r]);
-    mx = max_x32(mx);
-    const float m_new = fmax_(m_run, mx * sl2);
-    if (any_lane(m_new > m_run)) {         // rescale only when a row max grows
-      const float alpha = exp2_(m_run - (m_new == kNegInf ? 0.0f : m_new));
+    mx = max_x32(mx) * sl2;
+    const bool up = mx > m_run + kLazyLog2;
+    if (any_lane(up)) {
+      const float m_new = up ? mx : m_run;
+      const float alpha = m_new == kNegInf ? 1.0f : exp2_(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] *= alpha;
+      if (pending) scale_p(pp, alpha);
       m_run = m_new;
     }
+  };
+  // P^T(t) = exp2(S(t) sl2 - m_run) as the MFMA B operand; row sums into l
+  auto expsum = [&](f32x16 (&s)[2], u32x4 (&pb)[4]) {
     const float nm = m_run == kNegInf ? 0.0f : -m_run;
-    float ls = 0.0f;
+    float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_(__builtin_fmaf(s[sb][r], sl2, nm));
-        s[sb][r] = p;
-        ls += p;
-      }
-    l_run += ls;
-    // P^T operands: k-step kk uses block kk>>1, registers 8*(kk&1) .. +7
+    for (int r = 0; r < 16; ++r) {
+      s[0][r] = exp2_(__builtin_fmaf(s[0][r], sl2, nm));
+      s[1][r] = exp2_(__builtin_fmaf(s[1][r], sl2, nm));
+      ls0 += s[0][r];
+      ls1 += s[1][r];
+    }
+    l_run += ls0 + ls1;
+    // k-step kk uses block kk>>1, registers 8*(kk&1) .. +7
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -379,9 +404,43 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
         pb[kk][e] = pack_bf16x2(s[kk >> 1][8 * (kk & 1) + 2 * e],
                                 s[kk >> 1][8 * (kk & 1) + 2 * e + 1]);
   };
+  // O^T += V^T(t-1) P^T(t-1): four independent accumulation chains (d
+  // blocks); the V^T operands are read two MFMAs ahead
+  auto pv = [&](int buf, const u32x4 (&pb)[4]) {
+    const char* vb = buf ? vt1 : vt0;
+    u32x4 af[16];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int r0 = 32 * (kk >> 1) + 16 * (kk & 1);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const u32x2 lo = tr_read(vb + voff[db] + r0 * kRowBytes);
+        const u32x2 hi = tr_read(vb + voff[db] + (r0 + 8) * kRowBytes);
+        af[4 * kk + db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(af[4 * kk + db]), as_bf(pb[kk]),
+                                                        o[db], 0, 0, 0);
+  };
+  // pattern of a P V block: V^T reads two MFMAs ahead, and `valu` vector ALU
+  // instructions (the next tile's exponentials) after each MFMA
+  auto pv_schedule = [&](auto valu) {
+    constexpr int NV = decltype(valu)::value;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 1);
+    }
+  };
 
   f32x16 s[2];
-  u32x4 pb[4];
+  u32x4 pa[4], pn[4];   // P^T of the previous tile / of this tile
   // iteration t uses K buffer t&1 and V buffer (t-1)&1; `par` = t&1
   __amdgpu_buffer_rsrc_t rk_next = block_rsrc(0, kbase);
   __amdgpu_buffer_rsrc_t rv_cur = block_rsrc(0, vbase);
@@ -397,9 +456,24 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
       stage(t + 1, true, P ^ 1, rk_next);
     }
     if (t < ntiles) stage(t, false, P, rv_cur);
-    if (t < t_act) qk(P, s);
-    if (t >= 1 && t - 1 < t_act) pv(P ^ 1, pb);
-    if (t < t_act) softmax(t, s, pb);
+    const bool pending = t >= 1 && t - 1 < t_act;   // P(t-1) V(t-1) still to add
+    if (t < t_act) {
+      qk(P, s);
+      if (t >= t_mask) mask_tile(t, s);
+      update_max(s, pending, pa);
+      if (pending) {
+        pv(P ^ 1, pa);
+        expsum(s, pn);
+        pv_schedule(std::integral_constant<int, 7>{});
+      } else {
+        expsum(s, pn);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) pa[kk] = pn[kk];
+    } else if (pending) {
+      pv(P ^ 1, pa);
+      pv_schedule(std::integral_constant<int, 0>{});
+    }
     if (t + 1 < ntiles) rv_cur = block_rsrc(t + 1, vbase);
   };
   for (int t = 0; t <= ntiles; t += 2) {
