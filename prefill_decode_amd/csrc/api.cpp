@@ -223,6 +223,7 @@ KernelArgs make_args(const pod_attn_plan_s* pl, const pod_attn_tensors_t* t, con
   a.hq = p.num_qo_heads;
   a.hkv = p.num_kv_heads;
   a.group = p.num_qo_heads / p.num_kv_heads;
+  a.p_heads = prefill_heads(a.group);
   int sh = 0;
   if (p.kv_layout == POD_KV_PAGED)
     while ((1 << sh) < p.page_size) ++sh;

@@ -55,6 +55,7 @@ struct KernelArgs {
   int32_t num_pools;
   int32_t pool_off[kMaxPools + 1];
   int32_t hq, hkv, group;
+  int32_t p_heads;        // query heads per prefill item (prefill_heads(group))
   int32_t page_shift;     // log2(page_size) when paged
   int32_t causal;
   float scale_log2;       // sm_scale * log2(e)

@@ -183,12 +183,18 @@ struct KvAddr {
 };
 
 // ---------------------------------------------------------------------------
-// Prefill: 128 query rows x one head over keys [kv_begin, kv_end), 64-key
-// tiles.  Iteration t: LDS DMA of K(t+1) and V(t) is issued, S(t) = K(t) Q^T
-// runs on the matrix cores, then O^T += V^T(t-1) P^T(t-1) (deferred one
-// tile, so that these MFMAs overlap the softmax of tile t on the VALU).
-// The loop is unrolled by two so that every LDS address is a per-lane base
-// plus an immediate offset.
+// Prefill item: positions pos0 .. pos0 + nrows - 1 of one request (q rows
+// qrow0 + i) for nh query heads head0 .. head0 + nh - 1 that share one KV
+// head, over keys [kv_begin, kv_end); 256 (position, head) rows in all.  Wave
+// w takes head head0 + w / (4 / nh) and 64 consecutive positions as two
+// 32-row MFMA blocks A and B, so that every K and V^T operand read from LDS
+// feeds two MFMAs, and one staged K/V tile serves all nh heads.
+//
+// Keys come in 64-key LDS tiles (double buffered, staged by LDS DMA), each
+// processed as two 32-key halves: S^T = K Q^T for blocks A and B (one K
+// operand, two MFMAs), the online softmax of both blocks, then O^T += V^T
+// P^T (one V^T operand, two MFMAs).  The loop over tiles is unrolled by two
+// so that every LDS address is a per-lane base plus an immediate offset.
 // ---------------------------------------------------------------------------
 template <int KVM>
 __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char* __restrict__ kt0,
@@ -203,10 +209,14 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   const int hl = lane >> 5;            // half of the wave
   const int l32 = lane & 31;
   const int g16 = lane >> 4, j16 = lane & 15;
-  const int qrow0 = it[P_QROW0], head = it[P_HEAD], nrows = it[P_NROWS];
+  const int qrow0 = it[P_QROW0], head0 = it[P_HEAD], nrows = it[P_NROWS];
   const int pos0 = it[P_POS0], kv_begin = it[P_KV_BEGIN], kv_end = it[P_KV_END];
   const int kvreq = it[P_KVREQ], part = it[P_PART];
-  const int kvh = head / a.group;
+  const int wph = kWavesPerWG / a.p_heads;          // waves per head
+  const int hidx = wave / wph;
+  const int wpos = kWaveRows * (wave - hidx * wph);  // first position (item-relative)
+  const int head = head0 + hidx;
+  const int kvh = head0 / a.group;
   const uint32_t tok = (uint32_t)a.hkv * kRowBytes;
   const char* kbase = (const char*)a.k + kvh * kRowBytes;
   const char* vbase = (const char*)a.v + kvh * kRowBytes;
@@ -217,36 +227,37 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   const int nfull = span / kPrefillKeys;
   const bool causal = a.causal != 0;
   const float sl2 = a.scale_log2;
-  const int wave_pos_lo = pos0 + wave * 32;         // smallest position of the wave
-  // tiles [0, t_act) hold a key visible to some row of this wave; tiles
-  // >= t_mask need per-element masking (split end or diagonal)
-  const int x_act = wave_pos_lo + 31 - kv_begin;
-  const int t_act = !causal ? ntiles : x_act < 0 ? 0 : min(ntiles, x_act / kPrefillKeys + 1);
-  const int t_mask = causal ? min(nfull, max(0, (wave_pos_lo - kv_begin + 1) / kPrefillKeys))
-                            : nfull;
+  // keys this wave needs: tiles [0, t_act); tiles >= t_mask need masking
+  const int nvalid = min(kWaveRows, nrows - wpos);  // may be <= 0
+  const int pos_lo = pos0 + wpos;
+  const int pos_hi = pos_lo + max(nvalid, 1) - 1;
+  const int x_act = pos_hi - kv_begin;
+  const int t_act = nvalid <= 0 ? 0
+                    : !causal    ? ntiles
+                    : x_act < 0  ? 0
+                                 : min(ntiles, x_act / kPrefillKeys + 1);
+  const int t_mask = causal ? min(nfull, max(0, (pos_lo - kv_begin + 1) / kPrefillKeys)) : nfull;
 
-  // Q^T operand: lane holds row (wave*32 + l32), d = 16*kk + 8*hl + e
-  const int row = wave * 32 + l32;
-  const bool row_ok = row < nrows;
-  const int qpos = pos0 + row;                      // this lane's query position
-  u32x4 qf[8];
+  // Q^T operands of blocks A (positions wpos + l32) and B (+32):
+  // lane holds d = 16 kk + 8 hl + e
+  const int rA = wpos + l32, rB = rA + 32;          // item-relative positions
+  const bool okA = rA < nrows, okB = rB < nrows;
+  u32x4 qa[8], qb[8];
   {
-    const uint16_t* qp = a.q_prefill +
-        ((int64_t)(qrow0 + (row_ok ? row : 0)) * a.hq + head) * kHeadDim + 8 * hl;
+    const uint16_t* qpa = a.q_prefill +
+        ((int64_t)(qrow0 + (okA ? rA : 0)) * a.hq + head) * kHeadDim + 8 * hl;
+    const uint16_t* qpb = a.q_prefill +
+        ((int64_t)(qrow0 + (okB ? rB : 0)) * a.hq + head) * kHeadDim + 8 * hl;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qf[kk] = row_ok ? *(const u32x4*)(qp + 16 * kk) : u32x4{0, 0, 0, 0};
+    for (int kk = 0; kk < 8; ++kk) {
+      qa[kk] = okA ? *(const u32x4*)(qpa + 16 * kk) : u32x4{0, 0, 0, 0};
+      qb[kk] = okB ? *(const u32x4*)(qpb + 16 * kk) : u32x4{0, 0, 0, 0};
+    }
   }
 
   // staging: wave w fills rows [16w, 16w + 16) of a tile, four rows per
   // instruction; lane L deposits row 4i + L/16, chunk position L%16, which
   // holds source chunk (L%16) ^ swizzle(row)
-  const int dq = lane >> 4, dc = lane & 15;
-  uint32_t voffk[4], voffv[2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) voffk[i] = dq * tok + 16u * (dc ^ kswz(4 * i + dq));
-#pragma unroll
-  for (int i = 0; i < 2; ++i) voffv[i] = dq * tok + 16u * (dc ^ vswz(4 * i + dq));
   const int wrow = 16 * wave * kRowBytes;           // this wave's rows in a tile
   // A tile's 16-key blocks each lie in one page (page_size >= 16); in the
   // last, partial tile the blocks and the lanes' rows are clamped to the last
@@ -254,13 +265,21 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   const int lastb = (kv_end - 1) & ~15;             // start of the block holding key kv_end-1
   auto bstart = [&](int t) { return min(kv_begin + t * kPrefillKeys + 16 * wave, lastb); };
   auto stage = [&](int t, bool is_k, int buf, __amdgpu_buffer_rsrc_t r) {
+    // lane-derived offsets are recomputed here rather than held across the
+    // tile loop (registers are the limit of this kernel)
+    int sl = threadIdx.x;
+    asm volatile("" : "+v"(sl));
+    const int dq = (sl >> 4) & 3, dc = sl & 15, lane = sl & 63;
     char* dst = (is_k ? (buf ? kt1 : kt0) : (buf ? vt1 : vt0)) + wrow;
     if (KVM != KV_PAGED_NARROW) {
       const int rmax = kv_end - 1 - bstart(t);
       if (rmax >= 15) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dma16(r, dst + 4 * i * kRowBytes, is_k ? voffk[i] : voffv[i & 1], 4 * i * tok);
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 4 * i + dq;
+          const uint32_t vo = dq * tok + 16u * (dc ^ (is_k ? kswz(rr) : vswz(rr)));
+          dma16(r, dst + 4 * i * kRowBytes, vo, 4 * i * tok);
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -288,229 +307,211 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
     return rsrc(gbase + (KVM != KV_PAGED_NARROW ? addr.block_row(bstart(t)) : 0) * tok);
   };
 
-  // per-lane LDS read offsets (bytes from a tile's base)
-  // K rows 32 sb + l32, chunk (2 kk + hl) ^ swz; sb and the buffer are immediates
-  uint32_t koff[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    koff[kk] = (uint32_t)(l32 * kRowBytes + 16 * ((2 * kk + hl) ^ kswz(l32)));
-  // V^T reads: rows vrow0 + 32 (kk>>1) + 16 (kk&1) (+8), chunk 4 db + .. ^ swz
+  // per-lane LDS read offsets (bytes from a tile's base); the half h and
+  // the buffer are immediates.  K: row 32 h + l32, chunk (2 kk + hl) ^ swz =
+  // 2 (kk ^ (swz >> 1)) + (hl ^ (swz & 1)).
+  const int ksw = kswz(l32);
+  const uint32_t kofs0 = (uint32_t)(l32 * kRowBytes + 16 * (hl ^ (ksw & 1)));
+  const uint32_t kx = (uint32_t)(ksw >> 1);
+  // (the per-read offsets are formed from these inside each half; held
+  // for the whole loop they would not fit the register file)
+  // V^T: rows vrow0 + 32 h + 16 ks (+8), chunk (4 db + c) ^ swz =
+  // 4 (db ^ (swz >> 2)) + (c ^ (swz & 3))
   const int vrow0 = 4 * hl + (j16 >> 2);
   const int vsw = vswz(vrow0);
-  uint32_t voff[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-    voff[db] = (uint32_t)(vrow0 * kRowBytes +
-                          16 * ((4 * db + 2 * (g16 & 1) + ((j16 & 3) >> 1)) ^ vsw) + 8 * (j16 & 1));
+  const uint32_t vofs0 = (uint32_t)(vrow0 * kRowBytes +
+                                    16 * ((2 * (g16 & 1) + ((j16 & 3) >> 1)) ^ (vsw & 3)) +
+                                    8 * (j16 & 1));
+  const uint32_t vx = (uint32_t)(vsw >> 2);
 
-  // S^T(t) = K(t) Q^T: two key blocks' accumulation chains interleaved so
-  // that consecutive MFMAs are independent; eight K operand reads (four
-  // k-steps) are kept in flight ahead of the MFMAs.
-  auto qk = [&](int buf, f32x16 (&s)[2]) {
-    const char* kb = buf ? kt1 : kt0;
-    u32x4 ka[8], kc[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      ka[kk] = *(const u32x4*)(kb + koff[kk]);
-      kc[kk] = *(const u32x4*)(kb + koff[kk] + 32 * kRowBytes);
-    }
-    f32x16 a0 = {}, a1 = {};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(ka[kk]), as_bf(qf[kk]), a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kc[kk]), as_bf(qf[kk]), a1, 0, 0, 0);
-    }
-    // 8 reads up front, then per k-step: 2 MFMAs, the 2 reads of k-step + 4
-#pragma unroll
-    for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      if (kk < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    s[0] = a0;
-    s[1] = a1;
-  };
-  f32x16 o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
-  // Online softmax with a lazy reference max: a row's reference m_run moves
-  // only when the row max exceeds it by more than kLazyLog2, so that P =
-  // exp2(s - m_run) <= 2^kLazyLog2 (exact in fp32, one bf16 rounding as any
-  // P) and the rescale of O -- which would have to wait for the previous
-  // tile's P V product -- is rare.  O / l are normalised by the same m_run at
-  // the end, so the result is the softmax either way.
+  f32x16 oa[4], ob[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    oa[i] = f32x16{};
+    ob[i] = f32x16{};
+  }
+  // Online softmax with a lazy reference max: a row's reference m moves only
+  // when the row max exceeds it by more than kLazyLog2, so P = exp2(s - m) <=
+  // 2^kLazyLog2 (exact in fp32, one bf16 rounding as any P) and the rescale
+  // of O is rare.  O / l are normalised by the same m at the end, so the
+  // result is the softmax either way.
   constexpr float kLazyLog2 = 8.0f;
-  float m_run = kNegInf, l_run = 0.0f;
-  auto mask_tile = [&](int t, f32x16 (&s)[2]) {
-    const int k0 = kv_begin + t * kPrefillKeys + 4 * hl;
+  float ma = kNegInf, la = 0.0f, mb = kNegInf, lb = 0.0f;
+
+  // S^T of one 32-key half for both blocks: one K operand, two MFMAs
+  auto qk = [&](const char* kb, uint32_t k0, uint32_t kxx, f32x16& sa, f32x16& sb) {
+    auto koff = [&](int kk) { return k0 + 32u * ((uint32_t)kk ^ kxx); };
+    sa = f32x16{};
+    sb = f32x16{};
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int kk = 0; kk < 8; ++kk) {
+      const u32x4 kop = *(const u32x4*)(kb + koff(kk));
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kop), as_bf(qa[kk]), sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kop), as_bf(qb[kk]), sb, 0, 0, 0);
+    }
+    // K operand reads one k-step ahead of their MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * sb + 8 * (r >> 2) + (r & 3);
-        if (key >= kv_end || (causal && key > qpos)) s[sb][r] = kNegInf;
-      }
+    for (int kk = 0; kk < 8; ++kk) {
+      if (kk < 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
   };
-  // scale a pending P^T operand (bf16 pairs) by the lane's alpha
-  auto scale_p = [&](u32x4 (&p)[4], float alpha) {
+  // register r holds key key0 + 8 (r >> 2) + (r & 3) (key0 includes 4 hl);
+  // keys below `lim` are visible: r is kept iff its offset < lim - key0
+  auto mask = [&](f32x16& sx, int key0, int lim) {
+    const int dd = lim - key0;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w = p[kk][e];
-        p[kk][e] = pack_bf16x2(__uint_as_float(w << 16) * alpha,
-                               __uint_as_float(w & 0xFFFF0000u) * alpha);
-      }
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + (r & 3) >= dd) sx[r] = kNegInf;
   };
-  // row max of S(t); moves m_run (and rescales O, l and the pending P) when
-  // some row's max has grown past the lazy bound
-  auto update_max = [&](f32x16 (&s)[2], bool pending, u32x4 (&pp)[4]) {
-    float mx = kNegInf;
+  // row max of a block's S; moves m (and rescales O, l) past the lazy bound
+  auto update_max = [&](const f32x16& sx, float& m, float& l, f32x16 (&o)[4]) {
+    float mx = sx[0];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmax_(mx, s[sb][r]);
+    for (int r = 1; r < 16; ++r) mx = fmax_(mx, sx[r]);
     mx = max_x32(mx) * sl2;
-    const bool up = mx > m_run + kLazyLog2;
+    const bool up = mx > m + kLazyLog2;
     if (any_lane(up)) {
-      const float m_new = up ? mx : m_run;
-      const float alpha = m_new == kNegInf ? 1.0f : exp2_(m_run - m_new);
-      l_run *= alpha;
+      const float m_new = up ? mx : m;
+      const float alpha = m_new == kNegInf ? 1.0f : exp2_(m - m_new);
+      l *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] *= alpha;
-      if (pending) scale_p(pp, alpha);
-      m_run = m_new;
+      m = m_new;
     }
   };
-  // P^T(t) = exp2(S(t) sl2 - m_run) as the MFMA B operand; row sums into l
-  auto expsum = [&](f32x16 (&s)[2], u32x4 (&pb)[4]) {
-    const float nm = m_run == kNegInf ? 0.0f : -m_run;
-    float ls0 = 0.0f, ls1 = 0.0f;
+  // P^T = exp2(S sl2 - m) as two MFMA B operands (k-steps of 16 keys); row
+  // sum into l.  k-step ks uses registers 8 ks .. 8 ks + 7.
+  auto expsum = [&](f32x16& sx, float m, float& l, u32x4 (&p)[2]) {
+    const float nm = m == kNegInf ? 0.0f : -m;
+    float ls = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s[0][r] = exp2_(__builtin_fmaf(s[0][r], sl2, nm));
-      s[1][r] = exp2_(__builtin_fmaf(s[1][r], sl2, nm));
-      ls0 += s[0][r];
-      ls1 += s[1][r];
+      sx[r] = exp2_(__builtin_fmaf(sx[r], sl2, nm));
+      ls += sx[r];
     }
-    l_run += ls0 + ls1;
-    // k-step kk uses block kk>>1, registers 8*(kk&1) .. +7
+    l += ls;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pb[kk][e] = pack_bf16x2(s[kk >> 1][8 * (kk & 1) + 2 * e],
-                                s[kk >> 1][8 * (kk & 1) + 2 * e + 1]);
+      for (int e = 0; e < 4; ++e) p[ks][e] = pack_bf16x2(sx[8 * ks + 2 * e], sx[8 * ks + 2 * e + 1]);
   };
-  // O^T += V^T(t-1) P^T(t-1): four independent accumulation chains (d
-  // blocks); the V^T operands are read two MFMAs ahead
-  auto pv = [&](int buf, const u32x4 (&pb)[4]) {
-    const char* vb = buf ? vt1 : vt0;
-    u32x4 af[16];
+  // O^T += V^T P^T for one 32-key half: one V^T operand, two MFMAs
+  auto pv = [&](const char* vb, uint32_t v0, uint32_t vxx, const u32x4 (&pa)[2],
+                const u32x4 (&pb)[2]) {
+    auto voff = [&](int db) { return v0 + 64u * ((uint32_t)db ^ vxx); };
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int r0 = 32 * (kk >> 1) + 16 * (kk & 1);
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const u32x2 lo = tr_read(vb + voff[db] + r0 * kRowBytes);
-        const u32x2 hi = tr_read(vb + voff[db] + (r0 + 8) * kRowBytes);
-        af[4 * kk + db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        const u32x2 lo = tr_read(vb + voff(db) + 16 * ks * kRowBytes);
+        const u32x2 hi = tr_read(vb + voff(db) + (16 * ks + 8) * kRowBytes);
+        const u32x4 vop = {lo[0], lo[1], hi[0], hi[1]};
+        oa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vop), as_bf(pa[ks]), oa[db], 0, 0, 0);
+        ob[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vop), as_bf(pb[ks]), ob[db], 0, 0, 0);
       }
+    // V^T operand reads (two per operand) one operand ahead of its MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(af[4 * kk + db]), as_bf(pb[kk]),
-                                                        o[db], 0, 0, 0);
   };
-  // pattern of a P V block: V^T reads two MFMAs ahead, and `valu` vector ALU
-  // instructions (the next tile's exponentials) after each MFMA
-  auto pv_schedule = [&](auto valu) {
-    constexpr int NV = decltype(valu)::value;
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 1);
+  // one 32-key half h of tile t (buffers K kb, V vb).  No instruction is
+  // scheduled across a half's boundaries: overlapping two halves would keep
+  // both halves' S and operands live, beyond the register file.
+  auto half = [&](int t, int h, const char* kb, const char* vb, bool masked) {
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t k0 = kofs0, kxx = kx, v0 = vofs0, vxx = vx;
+    asm volatile("" : "+v"(k0), "+v"(kxx), "+v"(v0), "+v"(vxx));
+    f32x16 sa, sb;
+    qk(kb + 32 * h * kRowBytes, k0, kxx, sa, sb);
+    if (masked) {
+      const int key0 = kv_begin + t * kPrefillKeys + 32 * h + 4 * hl;
+      const int qpos = pos0 + wpos + (threadIdx.x & 31);   // block A's row position
+      mask(sa, key0, causal ? min(qpos + 1, kv_end) : kv_end);
+      mask(sb, key0, causal ? min(qpos + 33, kv_end) : kv_end);
     }
+    update_max(sa, ma, la, oa);
+    update_max(sb, mb, lb, ob);
+    u32x4 pa[2], pb[2];
+    expsum(sa, ma, la, pa);
+    expsum(sb, mb, lb, pb);
+    pv(vb + 32 * h * kRowBytes, v0, vxx, pa, pb);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  f32x16 s[2];
-  u32x4 pa[4], pn[4];   // P^T of the previous tile / of this tile
-  // iteration t uses K buffer t&1 and V buffer (t-1)&1; `par` = t&1
-  __amdgpu_buffer_rsrc_t rk_next = block_rsrc(0, kbase);
-  __amdgpu_buffer_rsrc_t rv_cur = block_rsrc(0, vbase);
-  stage(0, true, 0, rk_next);
+  // iteration t: K(t) and V(t) are in LDS buffers t&1; DMA of tile t+1
+  // goes to the other buffers, which the barrier released
+  __amdgpu_buffer_rsrc_t rk = block_rsrc(0, kbase), rv = block_rsrc(0, vbase);
+  stage(0, true, 0, rk);
+  stage(0, false, 0, rv);
   auto body = [&](int t, auto par) {
     constexpr int P = decltype(par)::value;
     wait_vmem<0>();
-    __syncthreads();                       // K(t), V(t-1) in LDS; K(t-1), V(t-2) consumed
-    // DMA of K(t+1) and V(t) into the buffers the barrier released; they
-    // have a whole iteration to land
+    __syncthreads();                       // tile t landed; tile t-1's buffers free
     if (t + 1 < ntiles) {
-      rk_next = block_rsrc(t + 1, kbase);
-      stage(t + 1, true, P ^ 1, rk_next);
+      rk = block_rsrc(t + 1, kbase);
+      rv = block_rsrc(t + 1, vbase);
+      stage(t + 1, true, P ^ 1, rk);
+      stage(t + 1, false, P ^ 1, rv);
     }
-    if (t < ntiles) stage(t, false, P, rv_cur);
-    const bool pending = t >= 1 && t - 1 < t_act;   // P(t-1) V(t-1) still to add
     if (t < t_act) {
-      qk(P, s);
-      if (t >= t_mask) mask_tile(t, s);
-      update_max(s, pending, pa);
-      if (pending) {
-        pv(P ^ 1, pa);
-        expsum(s, pn);
-        pv_schedule(std::integral_constant<int, 7>{});
-      } else {
-        expsum(s, pn);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) pa[kk] = pn[kk];
-    } else if (pending) {
-      pv(P ^ 1, pa);
-      pv_schedule(std::integral_constant<int, 0>{});
+      const char* kb = P ? kt1 : kt0;
+      const char* vb = P ? vt1 : vt0;
+      // the second half is needed unless every key in it is beyond the
+      // wave's last position or the KV range
+      const int k1 = kv_begin + t * kPrefillKeys + 32;
+      const bool h1 = k1 < kv_end && (!causal || k1 <= pos_hi);
+      // one copy of the half's code (a masked and an unmasked copy would
+      // double the live ranges the register allocator has to cover)
+      const bool masked = t >= t_mask;
+      half(t, 0, kb, vb, masked);
+      if (h1) half(t, 1, kb, vb, masked);
     }
-    if (t + 1 < ntiles) rv_cur = block_rsrc(t + 1, vbase);
   };
-  for (int t = 0; t <= ntiles; t += 2) {
+  for (int t = 0; t < ntiles; t += 2) {
     body(t, std::integral_constant<int, 0>{});
-    if (t + 1 <= ntiles) body(t + 1, std::integral_constant<int, 1>{});
+    if (t + 1 < ntiles) body(t + 1, std::integral_constant<int, 1>{});
   }
 
-  // epilogue: lanes l and l^32 hold the same query row
-  const float l_tot = sum_x32(l_run);
-  if (!row_ok) return;
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse2 = l_tot > 0.0f ? m_run + log2_(l_tot) : kNegInf;
-  if (part < 0) {
-    uint16_t* op = a.o_prefill + ((int64_t)(qrow0 + row) * a.hq + head) * kHeadDim + 4 * hl;
+  // epilogue: lanes l and l^32 hold the same query row of a block
+  auto finish = [&](const f32x16 (&o)[4], float m, float l, bool ok, int r) {
+    const float l_tot = sum_x32(l);
+    if (!ok) return;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float lse2 = l_tot > 0.0f ? m + log2_(l_tot) : kNegInf;
+    if (part < 0) {
+      uint16_t* op = a.o_prefill + ((int64_t)(qrow0 + r) * a.hq + head) * kHeadDim + 4 * hl;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const u32x2 w = {pack_bf16x2(o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv),
-                         pack_bf16x2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv)};
-        *(u32x2*)(op + 32 * db + 8 * g4) = w;
-      }
-    if (hl == 0 && a.lse_prefill)
-      a.lse_prefill[(int64_t)(qrow0 + row) * a.hq + head] = lse2 * kLn2;
-  } else {
-    const int pi = part + row;
-    float* pp = a.part_o + (int64_t)pi * kHeadDim + 4 * hl;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const u32x2 w = {pack_bf16x2(o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv),
+                           pack_bf16x2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv)};
+          *(u32x2*)(op + 32 * db + 8 * g4) = w;
+        }
+      if (hl == 0 && a.lse_prefill)
+        a.lse_prefill[(int64_t)(qrow0 + r) * a.hq + head] = lse2 * kLn2;
+    } else {
+      const int pi = part + hidx * (kPrefillRows / a.p_heads) + r;
+      float* pp = a.part_o + (int64_t)pi * kHeadDim + 4 * hl;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 w = {o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv,
-                         o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv};
-        *(f32x4*)(pp + 32 * db + 8 * g4) = w;
-      }
-    if (hl == 0) a.part_lse[pi] = lse2;
-  }
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 w = {o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv,
+                           o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv};
+          *(f32x4*)(pp + 32 * db + 8 * g4) = w;
+        }
+      if (hl == 0) a.part_lse[pi] = lse2;
+    }
+  };
+  finish(oa, ma, la, okA, rA);
+  finish(ob, mb, lb, okB, rB);
 }
 
 // ---------------------------------------------------------------------------

@@ -124,18 +124,20 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
   WorkLists w;
   int32_t n_partials = 0;
 
-  // ---- prefill tiles (request, query head, 128-row block) ----
+  // ---- prefill items (request, group of nh query heads, block of npos
+  // positions); nh * npos = kPrefillRows ----
+  const int32_t nh = prefill_heads(g), npos = prefill_positions(g);
   struct Tile { int32_t qrow0, head, nrows, pos0, kv_end, req, kvh; };
   std::vector<Tile> tiles;
   int32_t qrow = 0;
   for (int32_t r = 0; r < np; ++r) {
     const int32_t qo = b.qo[r], kv = b.pkv[r];
-    for (int32_t h = 0; h < hq; ++h)
-      for (int32_t r0 = 0; r0 < qo; r0 += kPrefillRows) {
+    for (int32_t h = 0; h < hq; h += nh)
+      for (int32_t r0 = 0; r0 < qo; r0 += npos) {
         Tile t;
         t.qrow0 = qrow + r0;
         t.head = h;
-        t.nrows = std::min(kPrefillRows, qo - r0);
+        t.nrows = std::min(npos, qo - r0);
         t.pos0 = kv - qo + r0;
         t.kv_end = p.causal ? std::min(kv, t.pos0 + t.nrows) : kv;
         t.req = r;
@@ -167,12 +169,13 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
     if (s > 1) {
       base = n_partials;
       n_partials += s * kPrefillRows;
-      for (int32_t i = 0; i < t.nrows; ++i) {
-        w.m_tasks.push_back((t.qrow0 + i) * hq + t.head);
-        w.m_tasks.push_back(base + i);
-        w.m_tasks.push_back(kPrefillRows);
-        w.m_tasks.push_back(s);
-      }
+      for (int32_t j = 0; j < nh; ++j)
+        for (int32_t i = 0; i < t.nrows; ++i) {
+          w.m_tasks.push_back((t.qrow0 + i) * hq + t.head + j);
+          w.m_tasks.push_back(base + j * npos + i);
+          w.m_tasks.push_back(kPrefillRows);
+          w.m_tasks.push_back(s);
+        }
     }
     w.p_splits_max = std::max(w.p_splits_max, s);
     for (int32_t k = 0; k < s; ++k) {

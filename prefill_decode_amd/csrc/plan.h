@@ -19,7 +19,8 @@ namespace pod {
 
 // Tile shapes shared by planner and kernels.
 constexpr int kHeadDim = 128;
-constexpr int kPrefillRows = 128;   // query rows per prefill workgroup (4 waves x 32)
+constexpr int kPrefillRows = 256;   // (position, head) rows per prefill item (4 waves x 64)
+constexpr int kWaveRows = 64;       // rows per wave: two 32-row MFMA blocks
 constexpr int kPrefillKeys = 64;    // keys per prefill KV tile
 constexpr int kDecodeStep = 32;     // keys per decode step (2 MFMA key blocks)
 constexpr int kDecodeRows = 16;     // decode query tile (MFMA 16 rows)
@@ -33,14 +34,15 @@ constexpr int kSeqDecodeUnitsPerWave = 2;     // sequential: one wave per unit, 
 
 // Prefill work item (8 int32).
 enum PItem : int {
-  P_QROW0 = 0,    // global row of q_prefill holding the tile's first row
-  P_HEAD = 1,     // query head
-  P_NROWS = 2,    // valid rows, 1..kPrefillRows
+  P_QROW0 = 0,    // global row of q_prefill holding the item's first position
+  P_HEAD = 1,     // first query head; the item covers prefill_heads(g) heads
+  P_NROWS = 2,    // valid positions, 1..kPrefillRows / prefill_heads(g)
   P_POS0 = 3,     // absolute position of the first row (kv_len - qo_len + row)
   P_KV_BEGIN = 4, // first key of this split (multiple of kPrefillKeys)
   P_KV_END = 5,   // one past the last key this split may read
   P_KVREQ = 6,    // request index into kv_indptr / page_indptr
-  P_PART = 7,     // -1: write O/LSE; else partial index of row 0 (row i: +i)
+  P_PART = 7,     // -1: write O/LSE; else partial index of row 0, where the
+                  // row of (head slot j, position i) is j * positions + i
   P_FIELDS = 8
 };
 
@@ -65,6 +67,15 @@ enum MTask : int {
   M_NFLAG = 3,    // n_splits | (is_decode << 16)
   M_FIELDS = 4
 };
+
+// Query heads packed into one prefill item (they share one KV head, so one
+// staged K/V tile serves all of them): 4, 2 or 1, the largest dividing the
+// group size Hq / Hkv.
+inline int32_t prefill_heads(int32_t group) {
+  return group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+}
+// positions per prefill item
+inline int32_t prefill_positions(int32_t group) { return kPrefillRows / prefill_heads(group); }
 
 struct WorkLists {
   std::vector<int32_t> p_items;    // P_FIELDS each, grouped by XCD pool

@@ -133,5 +133,6 @@ def test_host_plan_cannot_run_and_null_handles():
     assert lib.pod_attn_probe_hwid(0, None, None) == INV
     lib.pod_attn_plan_destroy(None)   # no-op
     info = pl.info()
-    assert info["workspace_bytes"] > 0 and info["prefill_items"] == 8   # 8 heads x 1 block
+    # 8 q heads over 2 KV heads: two items of 4 packed heads x 1 position block
+    assert info["workspace_bytes"] > 0 and info["prefill_items"] == 2
     pl.destroy()

@@ -34,17 +34,21 @@ def _check_lists(spec, pitems, ditems, mtasks, pool_off, n_partials):
     M = mtasks.reshape(-1, M_F)
     used = np.zeros(max(n_partials, 1), dtype=np.int32)
 
-    # ---- prefill: group items by tile (qrow0, head) ----
+    # ---- prefill: group items by tile (qrow0, first head); a tile covers
+    # nh heads (4, 2 or 1: the largest dividing g) x up to 256 / nh positions
+    nh = 4 if g % 4 == 0 else 2 if g % 2 == 0 else 1
+    npos = 256 // nh
     tiles = {}
     for it in P:
         tiles.setdefault((int(it[0]), int(it[1])), []).append(it)
     covered = np.zeros((int(offs[-1]), hq), dtype=np.int32)
-    split_of_row = {}
     for (qrow0, h), its in tiles.items():
+        assert h % nh == 0 and h + nh <= hq
         its = sorted(its, key=lambda x: x[4])
         r = int(its[0][6])
         nrows, pos0 = int(its[0][2]), int(its[0][3])
         assert all(int(x[2]) == nrows and int(x[3]) == pos0 and int(x[6]) == r for x in its)
+        assert 1 <= nrows <= npos
         assert offs[r] <= qrow0 and qrow0 + nrows <= offs[r + 1]
         row_in_req = qrow0 - offs[r]
         assert pos0 == kv[r] - qo[r] + row_in_req            # bottom-right alignment
@@ -54,17 +58,16 @@ def _check_lists(spec, pitems, ditems, mtasks, pool_off, n_partials):
         for a, b in zip(its[:-1], its[1:]):
             assert int(a[5]) == int(b[4]) and int(b[4]) % 64 == 0
         assert all(int(x[4]) < int(x[5]) for x in its)
-        covered[qrow0:qrow0 + nrows, h] += 1
+        covered[qrow0:qrow0 + nrows, h:h + nh] += 1
         parts = [int(x[7]) for x in its]
         if len(its) == 1:
             assert parts == [-1]
         else:
             assert all(p >= 0 for p in parts)
             for p in parts:
-                assert np.all(used[p:p + nrows] == 0)
-                used[p:p + nrows] += 1
-            for i in range(nrows):
-                split_of_row[((qrow0 + i) * hq + h, 0)] = (parts[0] + i, parts, len(its))
+                for j in range(nh):           # head slot j: rows p + j * npos + i
+                    assert np.all(used[p + j * npos:p + j * npos + nrows] == 0)
+                    used[p + j * npos:p + j * npos + nrows] += 1
     assert np.all(covered == 1)
 
     # ---- decode: units partition heads x keys ----
@@ -154,7 +157,7 @@ def test_forced_splits_are_honoured():
     pl = _spec_lists(spec, prefill_kv_splits=4, decode_kv_splits=8)
     P = pl.export(0).reshape(-1, P_F)
     D = pl.export(1).reshape(-1, D_F)
-    assert len(P) == 8 * 4                      # 8 heads x 1 block x 4 splits
+    assert len(P) == 2 * 2 * 4                  # 2 groups of 4 heads x 2 blocks of 64 x 4 splits
     d0 = D[D[:, 0] == 0]
     assert len(d0) == 2 * 8                     # 2 kv heads x 8 splits
     d1 = D[D[:, 0] == 1]
