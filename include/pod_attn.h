@@ -64,19 +64,26 @@ typedef enum { POD_KV_CONTIGUOUS = 0, POD_KV_PAGED = 1 } pod_kv_layout_t;
 
 /* Scheduler modes of the fused kernel's per-CU counter. */
 typedef enum {
-  /* The counter holds the (prefill, decode) counts of the CU's workgroups;
-   * a starting workgroup takes the role that is below its target share. */
+  /* The CU's workgroups start together and take roles in arrival order: the
+   * first prefill_quarters/4 of them (in quarters, spread over neighbouring
+   * CUs) prefill, the rest decode. */
   POD_SCHED_LIVE = 0,
   /* The counter is a ticket: role = pattern[ticket % wgs_per_cu], the
    * prefill slots first ([POD] "Self-assign roles per SM in software"). */
   POD_SCHED_TICKET = 1,
   /* No role steering: every workgroup takes prefill units while they last,
    * then decode units (a fused launch without co-location control). */
-  POD_SCHED_ORDERED = 2
+  POD_SCHED_ORDERED = 2,
+  /* CU-level partition: every workgroup of a CU takes the same first role;
+   * prefill_quarters_per_cu / 8 of the CUs start on prefill tiles, the rest
+   * on decode units (each workgroup still moves to the other queue when its
+   * own runs dry). */
+  POD_SCHED_SPLIT = 3
 } pod_sched_mode_t;
 
 /* tuning flags */
-#define POD_FLAG_TRACE 0x1u   /* fused run records one pod_trace_record_t per unit */
+#define POD_FLAG_TRACE 0x1u   /* fused run (and, with match_sequential, sequential
+                                 run) records one pod_trace_record_t per unit */
 
 typedef struct pod_attn_plan_s* pod_attn_plan_t;   /* opaque, library-owned */
 

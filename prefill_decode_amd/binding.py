@@ -21,7 +21,7 @@ POD_OK = 0
 STATUS = {0: "POD_OK", 1: "POD_ERR_INVALID_ARGUMENT", 2: "POD_ERR_UNSUPPORTED",
           3: "POD_ERR_WORKSPACE_TOO_SMALL", 4: "POD_ERR_HIP", 5: "POD_ERR_INTERNAL"}
 KV_CONTIGUOUS, KV_PAGED = 0, 1
-SCHED_LIVE, SCHED_TICKET, SCHED_ORDERED = 0, 1, 2
+SCHED_LIVE, SCHED_TICKET, SCHED_ORDERED, SCHED_SPLIT = 0, 1, 2, 3
 FLAG_TRACE = 0x1
 
 # every function the header declares

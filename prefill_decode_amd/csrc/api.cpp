@@ -47,6 +47,7 @@ struct pod_attn_plan_s {
   // workspace layout (bytes)
   size_t off_counters = 0, off_trace = 0, off_part_lse = 0, off_part_o = 0;
   DevLists dl_fused, dl_seq;
+  uint64_t launches[2] = {0, 0};   // successful launches per kind (counter parity)
   size_t ws_bytes = 0;
   char* ws = nullptr;          // caller-owned device buffer (NULL: host-only plan)
   int device = -1;
@@ -88,12 +89,12 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   const int64_t fused_p_slots = sum_qo <= 1536 ? p_slots_coloc : slots;
   const int64_t fused_d_waves =
       std::max<int64_t>(kWavesPerWG, (int64_t)dev.num_cus * (4 * c.wgs_per_cu - c.prefill_quarters));
-  build_lists(pl->batch, dev, fused_p_slots, fused_d_waves, kFusedDecodeUnitsPerWave,
-              t.prefill_kv_splits, t.decode_kv_splits, &pl->fused);
+  build_lists(pl->batch, dev, fused_p_slots, kFusedPrefillItemsPerSlot, fused_d_waves,
+              kFusedDecodeUnitsPerWave, t.prefill_kv_splits, t.decode_kv_splits, &pl->fused);
   // Sequential plan: each kernel has the whole GPU.
   pl->seq_is_fused = t.match_sequential == 1;
   if (!pl->seq_is_fused)
-    build_lists(pl->batch, dev, slots, slots * kWavesPerWG, kSeqDecodeUnitsPerWave,
+    build_lists(pl->batch, dev, slots, 2, slots * kWavesPerWG, kSeqDecodeUnitsPerWave,
                 t.prefill_kv_splits, t.decode_kv_splits, &pl->seq);
   const WorkLists& sq = pl->seq_is_fused ? pl->fused : pl->seq;
   pl->n_partials = std::max(pl->fused.n_partials, sq.n_partials);
@@ -188,8 +189,26 @@ int kv_mode_of(const pod_attn_plan_s* pl) {
   return p.page_size >= 16 ? KV_PAGED_WIDE : KV_PAGED_NARROW;
 }
 
+// Counter blocks of a launch of `kind` on `stream`: alternate by launch
+// parity, or the self-resetting block while the stream is being captured.
+void pick_counters(pod_attn_plan_s* pl, int kind, hipStream_t stream, KernelArgs* a) {
+  int32_t* base = (int32_t*)(pl->ws + pl->off_counters) + kind * kBlocksPerKind * kCtrBlockInts;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) cs = hipStreamCaptureStatusNone;
+  if (cs != hipStreamCaptureStatusNone) {
+    a->counters = base + 2 * kCtrBlockInts;
+    a->counters_next = nullptr;
+    a->self_reset = 1;
+  } else {
+    const int par = (int)(pl->launches[kind] & 1);
+    a->counters = base + par * kCtrBlockInts;
+    a->counters_next = base + (par ^ 1) * kCtrBlockInts;
+    a->self_reset = 0;
+  }
+}
+
 KernelArgs make_args(const pod_attn_plan_s* pl, const pod_attn_tensors_t* t, const WorkLists& w,
-                     const DevLists& dl, int counter_block) {
+                     const DevLists& dl) {
   KernelArgs a;
   std::memset(&a, 0, sizeof(a));
   const auto& p = pl->batch.params;
@@ -209,16 +228,13 @@ KernelArgs make_args(const pod_attn_plan_s* pl, const pod_attn_tensors_t* t, con
   a.p_items = (const int32_t*)(pl->ws + dl.p_items);
   a.d_items = (const int32_t*)(pl->ws + dl.d_items);
   a.m_tasks = (const int32_t*)(pl->ws + dl.m_tasks);
-  int32_t* ctr = (int32_t*)(pl->ws + pl->off_counters);
-  a.counters = ctr + counter_block;
-  a.cu_counters = ctr + kCuCounterOff;
   a.trace = nullptr;
   a.n_p = w.n_p();
   a.n_d = w.n_d();
   a.n_groups = w.n_groups();
   a.n_m = w.n_m();
   a.num_pools = (int32_t)w.pool_off.size() - 1;
-  a.n_dq = a.num_pools;
+  a.n_dq = std::min(kMaxDecodeQueues, 4 * a.num_pools);
   for (int i = 0; i <= a.num_pools && i <= kMaxPools; ++i) a.pool_off[i] = w.pool_off[i];
   a.hq = p.num_qo_heads;
   a.hkv = p.num_kv_heads;
@@ -339,7 +355,8 @@ pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t
   pod_status_t st = check_tensors(pl, t);
   if (st != POD_OK) return st;
   const WorkLists& w = pl->fused;
-  KernelArgs a = make_args(pl, t, w, pl->dl_fused, kFusedBlock);
+  KernelArgs a = make_args(pl, t, w, pl->dl_fused);
+  pick_counters(pl, kKindFused, stream, &a);
   if (pl->trace_records) a.trace = (pod_trace_record_t*)(pl->ws + pl->off_trace);
   // persistent: wgs_per_cu workgroups per CU, fewer when there are fewer units
   const int64_t slots = (int64_t)pl->dev.num_cus * pl->choice.wgs_per_cu;
@@ -350,6 +367,7 @@ pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t
   if (grid > 0) {
     e = launch_fused(a, kv_mode_of(pl), grid, stream);
     if (e != hipSuccess) return hip_err(e, "fused kernel launch");
+    if (!a.self_reset) ++pl->launches[kKindFused];
   }
   if (after_fused && (e = hipEventRecord(after_fused, stream)) != hipSuccess)
     return hip_err(e, "hipEventRecord(after_fused)");
@@ -369,11 +387,17 @@ pod_status_t pod_attn_sequential_run(pod_attn_plan_t pl, const pod_attn_tensors_
   pod_status_t st = check_tensors(pl, t);
   if (st != POD_OK) return st;
   const WorkLists& w = pl->seq_is_fused ? pl->fused : pl->seq;
-  KernelArgs a = make_args(pl, t, w, pl->dl_seq, kSeqBlock);
+  KernelArgs a = make_args(pl, t, w, pl->dl_seq);
+  pick_counters(pl, kKindSeq, stream, &a);
+  // the trace is indexed by the fused lists' units, so only a plan-matched
+  // sequential run records it
+  if (pl->trace_records && pl->seq_is_fused)
+    a.trace = (pod_trace_record_t*)(pl->ws + pl->off_trace);
   const int kvm = kv_mode_of(pl);
   if (w.n_p() > 0) {
     hipError_t e = launch_prefill(a, kvm, w.n_p(), stream);
     if (e != hipSuccess) return hip_err(e, "prefill kernel launch");
+    if (!a.self_reset) ++pl->launches[kKindSeq];
   }
   if (w.n_groups() > 0) {
     hipError_t e = launch_decode(a, kvm, w.n_groups(), stream);

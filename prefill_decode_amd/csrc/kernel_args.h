@@ -10,22 +10,31 @@ namespace pod {
 
 constexpr int kMaxPools = 16;
 
-// Counter layout.  A run's claim and completion counters are device-scope
-// atomics, which the MI355X serialises per address (about 11 ns each, a few
-// hundred ns of latency); each hot counter therefore gets its own 4 KiB so
-// that counters of different XCDs proceed in parallel.
+// Counter layout.  A run's claim counters are device-scope atomics, which
+// the MI355X serialises per address (about 11 ns each, a few hundred ns of
+// latency); each hot counter therefore gets its own 4 KiB so that counters of
+// different XCDs proceed in parallel.
+//
+// Each kind of launch (fused, sequential prefill) has three blocks: launches
+// alternate between blocks 0 and 1 by a host-side launch count, and the first
+// workgroup of a launch zeroes the block the next launch will use, so no
+// completion counting is needed; block 2 serves launches recorded into a
+// graph (whose arguments are frozen), which count completions and let the
+// last workgroup reset the block.
 constexpr int kCtrStride = 1024;           // ints between two hot counters
+constexpr int kMaxDecodeQueues = 32;
 constexpr int CS_POOL = 0;                 // +pool: claims from prefill pool (< kMaxPools)
-constexpr int CS_DQ = 16;                  // +queue: claims from decode queue (< kMaxPools)
-constexpr int CS_DONE = 32;                // +g (8 groups by blockIdx % 8): finished WGs
-constexpr int CS_DONE_ALL = 40;            // groups whose WGs all finished
-constexpr int kCtrSlots = 41;
-constexpr int kCtrBlockInts = kCtrSlots * kCtrStride;
-constexpr int kFusedBlock = 0;             // fused kernel's counter block
-constexpr int kSeqBlock = kCtrBlockInts;   // sequential prefill kernel's block
-constexpr int kCuCounterOff = 2 * kCtrBlockInts;
-constexpr int kCuCounters = 2048;          // per-CU role counters (fused kernel)
-constexpr int kCounterInts = kCuCounterOff + kCuCounters;
+constexpr int CS_DQ = 16;                  // +queue: claims from decode queue (< kMaxDecodeQueues)
+constexpr int CS_DONE = 48;                // +g (8 groups by blockIdx % 8): finished WGs
+constexpr int CS_DONE_ALL = 56;            // groups whose WGs all finished
+constexpr int kCtrSlots = 57;
+constexpr int kCuCounters = 2048;          // per-CU role counters (fused kernel), one per
+constexpr int kCellStride = 16;            // 64-byte line each
+constexpr int kCuCounterOff = kCtrSlots * kCtrStride;
+constexpr int kCtrBlockInts = kCuCounterOff + kCuCounters * kCellStride;
+constexpr int kBlocksPerKind = 3;          // parity 0, parity 1, self-resetting
+constexpr int kKindFused = 0, kKindSeq = 1;
+constexpr int kCounterInts = 2 * kBlocksPerKind * kCtrBlockInts;
 
 // KV addressing modes (kernel template parameter).
 enum KvMode : int { KV_CONTIG = 0, KV_PAGED_WIDE = 1, KV_PAGED_NARROW = 2 };
@@ -47,9 +56,10 @@ struct KernelArgs {
   const int32_t* p_items;
   const int32_t* d_items;
   const int32_t* m_tasks;
-  int32_t* counters;      // the launch's counter block (fused or sequential)
-  int32_t* cu_counters;   // per-CU counters (fused)
-  int32_t n_dq;           // decode queues (one per XCD): queue q holds units q, q+n_dq, ..
+  int32_t* counters;      // the launch's counter block (hot counters, then per-CU cells)
+  int32_t* counters_next; // block the next launch of this kind uses: zeroed here (or NULL)
+  int32_t self_reset;     // 1: count completions, last workgroup resets `counters`
+  int32_t n_dq;           // decode queues (4 per XCD): queue q holds groups q, q+n_dq, ..
   pod_trace_record_t* trace;
   int32_t n_p, n_d, n_groups, n_m;
   int32_t num_pools;

@@ -617,6 +617,9 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
   // `more`, K(s+1) (8 loads) was requested after the DMA of V(s), so V(s) has
   // landed once at most 8 loads are outstanding.
   auto step = [&](int s, const u32x4 (&kr)[8], const char* vsrc, char* vnext, bool more) {
+    // nothing is scheduled across a step's boundaries: the next step's
+    // MFMAs hoisted into this one would wait for K loads still in flight
+    __builtin_amdgcn_sched_barrier(0);
     const int k0 = kb + s * kDecodeStep;
     f32x4 s0 = {}, s1 = {};
 #pragma unroll
@@ -678,6 +681,7 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
 #pragma unroll
     for (int db = 0; db < 8; ++db)
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(af[db]), as_bf(pb), o[db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // The steady-state loop covers step pairs that both have a successor, so
@@ -744,46 +748,69 @@ __device__ __forceinline__ int peek(int* c) {
 }
 
 // Prefill claim (one thread): the pool of this XCD first, then the others.
+// The pools' counters are read together first (one round trip), then an
+// atomic is spent only on a pool that still had items.
 __device__ __forceinline__ int claim_prefill(const KernelArgs& a, int xcc) {
-  for (int i = 0; i < a.num_pools; ++i) {
-    const int p = (xcc + i) % a.num_pools;
+  const int np = a.num_pools;
+  int seen[kMaxPools];
+#pragma unroll
+  for (int i = 0; i < kMaxPools; ++i)
+    seen[i] = i < np ? peek(hot(a, CS_POOL + (xcc + i) % np)) : 0;
+#pragma unroll
+  for (int i = 0; i < kMaxPools; ++i) {
+    if (i >= np) break;
+    const int p = (xcc + i) % np;
     const int n = a.pool_off[p + 1] - a.pool_off[p];
-    if (n <= 0) continue;
-    int* c = hot(a, CS_POOL + p);
-    if (peek(c) >= n) continue;
-    const int k = atomicAdd(c, 1);
+    if (seen[i] >= n) continue;
+    const int k = atomicAdd(hot(a, CS_POOL + p), 1);
     if (k < n) return a.pool_off[p] + k;
   }
   return -1;
 }
 
-// Decode claim (one wavefront, result uniform): units are ordered longest
-// first and dealt round-robin to n_dq queues (queue q: units q, q + n_dq, ..),
-// so every queue is balanced and longest first too.  Queue q0 (this XCD's)
-// first, then the others.
-__device__ __forceinline__ int claim_decode_from(const KernelArgs& a, int q0) {
-  const int nq = a.n_dq;
-  for (int i = 0; i < nq; ++i) {
+// Decode claim (one thread, for its workgroup): a group of kWavesPerWG
+// consecutive units of the longest-first list, one per wave.  Groups are
+// dealt round-robin to n_dq queues (queue q: groups q, q + n_dq, ..), so every
+// queue is balanced and longest first too; the caller's own queue q0 is
+// tried first.  The queues' counters are read together first (one round trip).
+// A workgroup's four waves start and end their units together, as in a grid
+// launch of one group per workgroup, which measured faster than units taken
+// one wave at a time (those keep every wave streaming to the very end).
+__device__ __forceinline__ int claim_decode_group(const KernelArgs& a, int q0) {
+  const int nq = a.n_dq, ng = a.n_groups;
+  int seen[kMaxDecodeQueues];
+#pragma unroll
+  for (int i = 0; i < kMaxDecodeQueues; ++i)
+    seen[i] = i < nq ? peek(hot(a, CS_DQ + (q0 + i) % nq)) : ng;
+#pragma unroll
+  for (int i = 0; i < kMaxDecodeQueues; ++i) {
+    if (i >= nq) break;
     const int q = (q0 + i) % nq;
-    int u = a.n_d;
-    if (__lane_id() == 0) {
-      int* c = hot(a, CS_DQ + q);
-      if (q + nq * peek(c) < a.n_d) u = q + nq * atomicAdd(c, 1);
-    }
-    u = rfl(u);
-    if (u < a.n_d) return u;
+    if (q + nq * seen[i] >= ng) continue;
+    const int g = q + nq * atomicAdd(hot(a, CS_DQ + q), 1);
+    if (g < ng) return g;
   }
   return -1;
 }
 
-// Last workgroup of a launch resets the launch's counters (and the per-CU
-// role counters), so the next run starts from zero.  Completion is counted in
-// two levels (8 groups by blockIdx, then the groups) to keep the per-address
-// atomic traffic low.  Every claim a workgroup made returned before it counts
-// itself done (each returned value was used), and each level's atomic is
-// issued after the previous one returned, so no memory fence is needed.
-__device__ __forceinline__ void finish_launch(const KernelArgs& a, bool reset_cu,
-                                              int* s_last) {
+// First workgroup of a launch: zero the counter block of the next launch of
+// this kind (not in use now; the previous user finished before this launch).
+__device__ __forceinline__ void zero_next_counters(const KernelArgs& a) {
+  if (a.counters_next == nullptr || blockIdx.x != 0) return;
+  for (int i = threadIdx.x; i < kCtrSlots; i += blockDim.x) a.counters_next[i * kCtrStride] = 0;
+  for (int i = threadIdx.x; i < kCuCounters; i += blockDim.x)
+    a.counters_next[kCuCounterOff + i * kCellStride] = 0;
+}
+
+// Self-resetting launches (recorded into a graph): the last workgroup resets
+// the counters, so that every replay starts from zero.  Completion is counted
+// in two levels (8 groups by blockIdx, then the groups) to keep the
+// per-address atomic traffic low.  Every claim a workgroup made returned
+// before it counts itself done (each returned value was used), and each
+// level's atomic is issued after the previous one returned, so no memory
+// fence is needed.
+__device__ __forceinline__ void finish_launch(const KernelArgs& a, int* s_last) {
+  if (!a.self_reset) return;
   __syncthreads();
   if (threadIdx.x == 0) {
     const int g = (int)blockIdx.x & 7;
@@ -799,9 +826,9 @@ __device__ __forceinline__ void finish_launch(const KernelArgs& a, bool reset_cu
   if (*s_last) {
     for (int i = threadIdx.x; i < kCtrSlots; i += blockDim.x)
       __hip_atomic_store(hot(a, i), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (reset_cu)
-      for (int i = threadIdx.x; i < kCuCounters; i += blockDim.x)
-        __hip_atomic_store(&a.cu_counters[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = threadIdx.x; i < kCuCounters; i += blockDim.x)
+      __hip_atomic_store(&a.counters[kCuCounterOff + i * kCellStride], 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -836,35 +863,29 @@ __device__ __forceinline__ void trace_unit(const KernelArgs& a, int rec, int rol
 // Fused kernel: one persistent launch of wgs_per_cu workgroups per CU.  A
 // workgroup reads which CU it landed on, takes its first role from that CU's
 // counter (prefill for its share of the CU's slots), and works through the
-// queue of that role: prefill tiles one workgroup at a time, decode units one
-// wavefront at a time (each wave claims its own next unit, no workgroup
-// barrier between units).  When its queue runs dry it moves to the other
-// queue, so no slot idles while work is left.
+// queue of that role: prefill tiles one workgroup at a time, decode units in
+// groups of four (one per wave).  When its queue runs dry it moves to the
+// other queue, so no slot idles while work is left.
 template <int KVM>
 __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
   POD_LDS_OBJECTS
   const int tid = threadIdx.x;
   const int wave = rfl(tid >> 6), lane = tid & 63;
+  zero_next_counters(a);
   if (tid == 0) {
     const int slot = cu_slot_id();
     int role;   // 0 prefill, 1 decode
-    int* cell = &a.cu_counters[slot];
+    int* cell = &a.counters[kCuCounterOff + slot * kCellStride];
     const int tp = (a.prefill_quarters + (slot & 3)) >> 2;   // prefill target of this CU
-    const int td = a.wgs_per_cu - tp;
-    if (a.sched_mode == POD_SCHED_LIVE) {
-      int old = __hip_atomic_load(cell, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      while (true) {
-        const int lp = old & 0xFFFF, ld = old >> 16;
-        // take the role whose count is furthest below its target share
-        role = (td <= 0) ? 0 : (tp <= 0) ? 1 : ((lp + 1) * td <= (ld + 1) * tp ? 0 : 1);
-        const int nw = old + (role == 0 ? 1 : (1 << 16));
-        const int got = atomicCAS(cell, old, nw);
-        if (got == old) break;
-        old = got;
-      }
-    } else if (a.sched_mode == POD_SCHED_TICKET) {
+    if (a.sched_mode == POD_SCHED_LIVE || a.sched_mode == POD_SCHED_TICKET) {
+      // the CU's workgroups start together: the ticket (arrival order on
+      // this CU) gives the first tp of them the prefill role
       const int t = atomicAdd(cell, 1);
       role = (t % a.wgs_per_cu) < tp ? 0 : 1;
+    } else if (a.sched_mode == POD_SCHED_SPLIT) {
+      // the CU index within its shader array (0..7 or 0..15) spreads the
+      // prefill CUs evenly over every array and die
+      role = (slot & 7) < a.prefill_quarters ? 0 : 1;
     } else {
       role = 0;
     }
@@ -879,6 +900,7 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
   // the first worker to finish, which a claim made ahead of time would not
   // honour); a claim costs well under 1% of a unit. ----
   auto prefill_phase = [&]() {
+    if (a.n_p == 0) return;
     while (true) {
       __syncthreads();   // the previous unit / phase is done with LDS and s_info
       if (tid == 0) s_info[2] = claim_prefill(a, xcc);
@@ -890,16 +912,23 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
       if (a.trace && tid == 0) trace_unit(a, u, 0, u, slot, t0);
     }
   };
-  // ---- decode units until the queues are empty, one per wavefront ----
+  // ---- decode unit groups until the queues are empty: one unit per wave ----
   auto decode_phase = [&]() {
-    __syncthreads();   // the previous phase is done with LDS
+    if (a.n_d == 0) return;
     POD_DECODE_BUFFERS(wave)
-    const int q0 = xcc % a.n_dq;
-    int u;
-    while ((u = claim_decode_from(a, q0)) >= 0) {
-      const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
-      decode_unit<KVM>(a, (cptr)a.d_items + u * D_FIELDS, db0, db1);
-      if (a.trace && lane == 0) trace_unit(a, a.n_p + u, 1, u, slot, t0);
+    const int q0 = (4 * xcc + (slot & 3)) % a.n_dq;   // one of this XCD's queues
+    while (true) {
+      __syncthreads();   // the previous group / phase is done with LDS and s_info
+      if (tid == 0) s_info[2] = claim_decode_group(a, q0);
+      __syncthreads();
+      const int g = rfl(s_info[2]);
+      if (g < 0) break;
+      const int u = g * kWavesPerWG + wave;
+      if (u < a.n_d) {
+        const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
+        decode_unit<KVM>(a, (cptr)a.d_items + u * D_FIELDS, db0, db1);
+        if (a.trace && lane == 0) trace_unit(a, a.n_p + u, 1, u, slot, t0);
+      }
     }
   };
   if (role0 == 0) {
@@ -909,19 +938,23 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
     decode_phase();
     prefill_phase();
   }
-  finish_launch(a, true, &s_info[4]);
+  finish_launch(a, &s_info[4]);
 }
 
 template <int KVM>
 __global__ __launch_bounds__(256, 2) void pod_prefill_kernel(KernelArgs a) {
   POD_LDS_OBJECTS
+  zero_next_counters(a);
   if (threadIdx.x == 0) s_info[0] = claim_prefill(a, cu_slot_id() >> 8);
   __syncthreads();
   const int unit = s_info[0];
   __syncthreads();
-  if (unit >= 0)
+  if (unit >= 0) {
+    const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
     prefill_tile<KVM>(a, (cptr)a.p_items + rfl(unit) * P_FIELDS, POD_PREFILL_BUFFERS);
-  finish_launch(a, false, &s_info[1]);
+    if (a.trace && threadIdx.x == 0) trace_unit(a, unit, 0, unit, cu_slot_id(), t0);
+  }
+  finish_launch(a, &s_info[1]);
 }
 
 template <int KVM>
@@ -931,7 +964,11 @@ __global__ __launch_bounds__(256, 2) void pod_decode_kernel(KernelArgs a) {
   const int wave = rfl(threadIdx.x >> 6);
   const int d = blockIdx.x * kWavesPerWG + wave;
   POD_DECODE_BUFFERS(wave)
-  if (d < a.n_d) decode_unit<KVM>(a, (cptr)a.d_items + d * D_FIELDS, db0, db1);
+  if (d < a.n_d) {
+    const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
+    decode_unit<KVM>(a, (cptr)a.d_items + d * D_FIELDS, db0, db1);
+    if (a.trace && (threadIdx.x & 63) == 0) trace_unit(a, a.n_p + d, 1, d, cu_slot_id(), t0);
+  }
 }
 
 __global__ __launch_bounds__(256) void pod_merge_kernel(KernelArgs a) {

@@ -88,7 +88,7 @@ pod_status_t validate(const pod_attn_params_t* p, int32_t np, const int32_t* qo,
                   t->prefill_quarters_per_cu);
     if (t->prefill_kv_splits < 0 || t->decode_kv_splits < 0)
       return fail(err, POD_ERR_INVALID_ARGUMENT, "negative forced split count");
-    if (t->sched_mode < 0 || t->sched_mode > POD_SCHED_ORDERED)
+    if (t->sched_mode < 0 || t->sched_mode > POD_SCHED_SPLIT)
       return fail(err, POD_ERR_INVALID_ARGUMENT, "sched_mode %lld invalid", t->sched_mode);
     if (t->match_sequential != 0 && t->match_sequential != 1)
       return fail(err, POD_ERR_INVALID_ARGUMENT, "match_sequential must be 0 or 1");
@@ -116,8 +116,8 @@ int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu) {
 }
 
 void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_slots,
-                 int64_t decode_wave_slots, int32_t d_units_per_slot, int32_t force_p_splits,
-                 int32_t force_d_splits, WorkLists* out) {
+                 int32_t p_items_per_slot, int64_t decode_wave_slots, int32_t d_units_per_slot,
+                 int32_t force_p_splits, int32_t force_d_splits, WorkLists* out) {
   const auto& p = b.params;
   const int32_t hq = p.num_qo_heads, hkv = p.num_kv_heads, g = hq / hkv;
   const int32_t np = (int32_t)b.qo.size(), nd = (int32_t)b.dkv.size();
@@ -154,8 +154,11 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
   if (force_p_splits > 0) {
     s_all = force_p_splits;
   } else if (!tiles.empty()) {
-    // [POD] "Cap prefill splitting": at most two waves of the slots.
-    s_all = (int32_t)std::max<int64_t>(1, (2 * prefill_slots) / (int64_t)tiles.size());
+    // [POD] "Cap prefill splitting": at most a few waves of the slots (two
+    // for a sequential launch; more for the fused one, whose prefill slots
+    // run beside decode and whose last items form its tail).
+    s_all = (int32_t)std::max<int64_t>(
+        1, (std::max(1, p_items_per_slot) * prefill_slots) / (int64_t)tiles.size());
     s_all = std::min(s_all, kMaxPrefillSplits);
   }
   struct PI { std::vector<int32_t> f; double work; };

@@ -29,8 +29,10 @@ constexpr int kMaxXcds = 16;
 constexpr int kMaxPrefillSplits = 16;
 constexpr int kMaxDecodeSplits = 64;
 constexpr int kMinDecodeChunk = 512;   // keys per decode split, lower bound
-constexpr int kFusedDecodeUnitsPerWave = 4;   // fused: units claimed per wave, dynamic
-constexpr int kSeqDecodeUnitsPerWave = 2;     // sequential: one wave per unit, grid order
+constexpr int kFusedDecodeUnitsPerWave = 2;   // decode units per decode wavefront slot
+constexpr int kSeqDecodeUnitsPerWave = 2;
+constexpr int kFusedPrefillItemsPerSlot = 4;  // fused: prefill KV splits aim at this many
+                                              // items per prefill slot (shorter tail)
 
 // Prefill work item (8 int32).
 enum PItem : int {
@@ -116,7 +118,8 @@ int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu);
 // decode requests are split until there are about `d_units_per_slot` units
 // per decode wavefront (chunks of at least kMinDecodeChunk keys).
 void build_lists(const Batch& b, const pod_device_desc_t& dev,
-                 int64_t prefill_slots, int64_t decode_wave_slots, int32_t d_units_per_slot,
-                 int32_t force_p_splits, int32_t force_d_splits, WorkLists* out);
+                 int64_t prefill_slots, int32_t p_items_per_slot, int64_t decode_wave_slots,
+                 int32_t d_units_per_slot, int32_t force_p_splits, int32_t force_d_splits,
+                 WorkLists* out);
 
 }  // namespace pod

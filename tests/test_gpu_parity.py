@@ -95,7 +95,7 @@ def test_fused_equals_matched_sequential_bitwise_and_sched_modes():
     b = inputs.make_batch_host(spec)
     ref = oracle.batch_attention(b)
     results = []
-    for mode in (B.SCHED_LIVE, B.SCHED_TICKET, B.SCHED_ORDERED):
+    for mode in (B.SCHED_LIVE, B.SCHED_TICKET, B.SCHED_ORDERED, B.SCHED_SPLIT):
         for q in (1, 4, 7):
             say(f"[bitwise] mode={mode} quarters={q}")
             t = B.make_tuning(match_sequential=1, sched_mode=mode, prefill_quarters_per_cu=q,
@@ -199,3 +199,33 @@ def test_hwid_probe_and_workspace_error():
                            C.c_void_p(ws.data_ptr()), need.value - 256, C.byref(need), None,
                            C.byref(h))
     assert st == 3 and not h.value
+
+
+def test_graph_replays_match_eager():
+    # A run recorded into a HIP graph uses the self-resetting counter block;
+    # every replay (with eager runs in between) must equal the eager result.
+    import torch
+    spec = reduced_specs()[4]
+    b = inputs.make_batch_host(spec)
+    r = B.BatchRunner(b)
+    ref = run_path(r, "fused")
+    compare(ref, oracle.batch_attention(b), "graph-eager")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        r.run()
+    torch.cuda.synchronize()
+    for i in range(3):
+        say(f"[graph] replay {i}")
+        for t in (r.o_prefill, r.o_decode, r.lse_prefill, r.lse_decode):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = r.outputs()
+        for k in ref:
+            assert np.array_equal(got[k], ref[k]), ("replay", i, k)
+        eager = run_path(r, "fused")
+        for k in ref:
+            assert np.array_equal(eager[k], ref[k]), ("eager after replay", i, k)

@@ -182,21 +182,29 @@ def test_split_cap_two_waves():
 
 def test_small_prefill_regime_accounts_for_colocated_decode():
     # [PR] "Limit kv split when prefill tokens <= 1536": the fused plan's
-    # prefill splits fill only the slots beside the co-located decode WGs.
+    # prefill splits fill only the slots beside the co-located decode WGs;
+    # above 1536 tokens every slot.  Fused plans aim at up to 4 items per
+    # slot, sequential plans at 2.
+    def per_tile_max(P):
+        per = {}
+        for r in P:
+            per[(int(r[0]), int(r[1]))] = per.get((int(r[0]), int(r[1])), 0) + 1
+        return len(per), max(per.values())
+
     spec = inputs.config_spec("batched")          # exactly 1536 prefill tokens
     pl = _spec_lists(spec)
-    info = pl.info()
-    q = info["prefill_quarters_per_cu"]
+    q = pl.info()["prefill_quarters_per_cu"]
     fused = pl.export(0).reshape(-1, P_F)
     seq = pl.export(3).reshape(-1, P_F)
-    tiles = len({(int(r[0]), int(r[1])) for r in fused})
+    tiles, fmax = per_tile_max(fused)
     coloc_slots = max(1, 256 * q // 4)
-    assert len(fused) <= max(tiles, 2 * coloc_slots) + tiles   # per-tile rounding
-    assert len(seq) >= len(fused)
-    # above 1536 tokens the cap uses every slot
+    assert fmax <= max(1, 4 * coloc_slots // tiles)
+    _, smax = per_tile_max(seq)
+    assert smax <= max(1, 2 * 512 // tiles)
     big = inputs.custom_spec("big", 32, 8, [(1600, 4096)], [2000] * 64, seed=3)
     pb = _spec_lists(big)
-    assert pb.info()["prefill_items"] == len(pb.export(3)) // P_F
+    tiles_b, fmax_b = per_tile_max(pb.export(0).reshape(-1, P_F))
+    assert fmax_b == min(16, max(1, 4 * 512 // tiles_b))   # every slot counts
 
 
 def test_proportional_mix():
