@@ -284,7 +284,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--quarters", type=int, default=-1, help="prefill quarters per CU (-1 auto)")
-    ap.add_argument("--sched", type=int, default=0, help="0 live, 1 ticket, 2 ordered")
+    ap.add_argument("--sched", type=int, default=0,
+                    help="0 auto, 1 co-locate on every CU, 2 ordered, 3 CU partition")
     ap.add_argument("--pmc-run", action="store_true")
     ap.add_argument("--summarize-pmc", default=None, metavar="DIR")
     ap.add_argument("--summarize-stats", default=None, metavar="DIR")

@@ -62,22 +62,25 @@ typedef enum {
 
 typedef enum { POD_KV_CONTIGUOUS = 0, POD_KV_PAGED = 1 } pod_kv_layout_t;
 
-/* Scheduler modes of the fused kernel's per-CU counter. */
+/* Scheduler modes of the fused kernel: how the two workgroups of each CU
+ * pick their first role (every workgroup moves to the other queue when its
+ * own runs dry, so all modes run every unit exactly once). */
 typedef enum {
-  /* The CU's workgroups start together and take roles in arrival order: the
-   * first prefill_quarters/4 of them (in quarters, spread over neighbouring
-   * CUs) prefill, the rest decode. */
-  POD_SCHED_LIVE = 0,
-  /* The counter is a ticket: role = pattern[ticket % wgs_per_cu], the
-   * prefill slots first ([POD] "Self-assign roles per SM in software"). */
-  POD_SCHED_TICKET = 1,
+  /* The planner's choice (currently POD_SCHED_SPLIT). */
+  POD_SCHED_AUTO = 0,
+  /* Co-location on every CU: the CU's workgroups take roles in arrival
+   * order (a per-CU ticket), the first prefill_quarters_per_cu / 4 of them
+   * (in quarters, spread over neighbouring CUs) prefill, the rest decode
+   * ([POD] "Self-assign roles per SM in software"). */
+  POD_SCHED_COLOCATE = 1,
   /* No role steering: every workgroup takes prefill units while they last,
    * then decode units (a fused launch without co-location control). */
   POD_SCHED_ORDERED = 2,
   /* CU-level partition: every workgroup of a CU takes the same first role;
    * prefill_quarters_per_cu / 8 of the CUs start on prefill tiles, the rest
-   * on decode units (each workgroup still moves to the other queue when its
-   * own runs dry). */
+   * on decode units.  On MI355X one wave per SIMD cannot keep the matrix
+   * cores busy, so prefill runs best two waves per SIMD on fewer CUs while
+   * decode saturates HBM from the others. */
   POD_SCHED_SPLIT = 3
 } pod_sched_mode_t;
 

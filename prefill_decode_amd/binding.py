@@ -21,7 +21,7 @@ POD_OK = 0
 STATUS = {0: "POD_OK", 1: "POD_ERR_INVALID_ARGUMENT", 2: "POD_ERR_UNSUPPORTED",
           3: "POD_ERR_WORKSPACE_TOO_SMALL", 4: "POD_ERR_HIP", 5: "POD_ERR_INTERNAL"}
 KV_CONTIGUOUS, KV_PAGED = 0, 1
-SCHED_LIVE, SCHED_TICKET, SCHED_ORDERED, SCHED_SPLIT = 0, 1, 2, 3
+SCHED_AUTO, SCHED_COLOCATE, SCHED_ORDERED, SCHED_SPLIT = 0, 1, 2, 3
 FLAG_TRACE = 0x1
 
 # every function the header declares
@@ -138,7 +138,7 @@ def make_params(num_qo_heads, num_kv_heads, layout="paged", page_size=16, causal
 
 
 def make_tuning(wgs_per_cu=0, prefill_quarters_per_cu=-1, prefill_kv_splits=0,
-                decode_kv_splits=0, match_sequential=0, sched_mode=SCHED_LIVE,
+                decode_kv_splits=0, match_sequential=0, sched_mode=SCHED_AUTO,
                 flags=0) -> Tuning:
     return Tuning(wgs_per_cu, prefill_quarters_per_cu, prefill_kv_splits, decode_kv_splits,
                   match_sequential, sched_mode, flags)

@@ -75,10 +75,10 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   pl->batch.dkv.assign(dkv, dkv + nd);
   PlanChoice& c = pl->choice;
   c.wgs_per_cu = 2;
-  c.sched_mode = t.sched_mode;
+  c.sched_mode = t.sched_mode == POD_SCHED_AUTO ? POD_SCHED_SPLIT : t.sched_mode;
   c.prefill_quarters = t.prefill_quarters_per_cu >= 0
                            ? std::min(t.prefill_quarters_per_cu, 4 * c.wgs_per_cu)
-                           : auto_prefill_quarters(pl->batch, c.wgs_per_cu);
+                           : auto_prefill_quarters(pl->batch, c.wgs_per_cu, c.sched_mode);
   int64_t sum_qo = 0;
   for (int32_t x : pl->batch.qo) sum_qo += x;
   // Fused plan.  [PR]: with <= 1536 prefill tokens the prefill split count is
@@ -120,7 +120,7 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   pl->off_part_lse = off;
   off = align_up(off + (size_t)pl->n_partials * sizeof(float));
   pl->off_part_o = off;
-  off = align_up(off + (size_t)pl->n_partials * kHeadDim * sizeof(float));
+  off = align_up(off + (size_t)pl->n_partials * kHeadDim * sizeof(uint16_t));
   pl->ws_bytes = off;
   return POD_OK;
 }
@@ -223,7 +223,7 @@ KernelArgs make_args(const pod_attn_plan_s* pl, const pod_attn_tensors_t* t, con
   a.o_decode = (uint16_t*)t->o_decode;
   a.lse_prefill = t->lse_prefill;
   a.lse_decode = t->lse_decode;
-  a.part_o = (float*)(pl->ws + pl->off_part_o);
+  a.part_o = (uint16_t*)(pl->ws + pl->off_part_o);
   a.part_lse = (float*)(pl->ws + pl->off_part_lse);
   a.p_items = (const int32_t*)(pl->ws + dl.p_items);
   a.d_items = (const int32_t*)(pl->ws + dl.d_items);

@@ -51,7 +51,7 @@ struct KernelArgs {
   uint16_t* o_decode;
   float* lse_prefill;
   float* lse_decode;
-  float* part_o;          // [n_partials, 128] fp32
+  uint16_t* part_o;       // [n_partials, 128] bf16 (each partial divided by its own l)
   float* part_lse;        // [n_partials] fp32, log2 domain
   const int32_t* p_items;
   const int32_t* d_items;

@@ -498,14 +498,14 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
         a.lse_prefill[(int64_t)(qrow0 + r) * a.hq + head] = lse2 * kLn2;
     } else {
       const int pi = part + hidx * (kPrefillRows / a.p_heads) + r;
-      float* pp = a.part_o + (int64_t)pi * kHeadDim + 4 * hl;
+      uint16_t* pp = a.part_o + (int64_t)pi * kHeadDim + 4 * hl;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 w = {o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv,
-                           o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv};
-          *(f32x4*)(pp + 32 * db + 8 * g4) = w;
+          const u32x2 w = {pack_bf16x2(o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv),
+                           pack_bf16x2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv)};
+          *(u32x2*)(pp + 32 * db + 8 * g4) = w;
         }
       if (hl == 0) a.part_lse[pi] = lse2;
     }
@@ -722,9 +722,13 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
     if (q4 == 0 && a.lse_decode) a.lse_decode[(int64_t)qi * a.hq + h0 + j] = lse2 * kLn2;
   } else {
     const int pi = part + j * pstride;
-    float* pp = a.part_o + (int64_t)pi * kHeadDim + 4 * q4;
+    uint16_t* pp = a.part_o + (int64_t)pi * kHeadDim + 4 * q4;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) *(f32x4*)(pp + 16 * db) = o[db] * inv;
+    for (int db = 0; db < 8; ++db) {
+      const u32x2 w = {pack_bf16x2(o[db][0] * inv, o[db][1] * inv),
+                       pack_bf16x2(o[db][2] * inv, o[db][3] * inv)};
+      *(u32x2*)(pp + 16 * db) = w;
+    }
     if (q4 == 0) a.part_lse[pi] = lse2;
   }
 }
@@ -877,7 +881,7 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
     int role;   // 0 prefill, 1 decode
     int* cell = &a.counters[kCuCounterOff + slot * kCellStride];
     const int tp = (a.prefill_quarters + (slot & 3)) >> 2;   // prefill target of this CU
-    if (a.sched_mode == POD_SCHED_LIVE || a.sched_mode == POD_SCHED_TICKET) {
+    if (a.sched_mode == POD_SCHED_COLOCATE) {
       // the CU's workgroups start together: the ticket (arrival order on
       // this CU) gives the first tp of them the prefill role
       const int t = atomicAdd(cell, 1);
@@ -985,9 +989,9 @@ __global__ __launch_bounds__(256) void pod_merge_kernel(KernelArgs a) {
     for (int s = 0; s < n; ++s) {
       const int pi = base + s * stride;
       const float wgt = exp2_(a.part_lse[pi] - m);   // 0 for an empty split
-      const float2 v = *(const float2*)(a.part_o + (int64_t)pi * kHeadDim + 2 * lane);
-      acc0 += wgt * v.x;
-      acc1 += wgt * v.y;
+      const uint32_t v = *(const uint32_t*)(a.part_o + (int64_t)pi * kHeadDim + 2 * lane);
+      acc0 += wgt * __uint_as_float(v << 16);
+      acc1 += wgt * __uint_as_float(v & 0xFFFF0000u);
       tot += wgt;
     }
   }

@@ -23,11 +23,13 @@ pod_status_t fail(std::string* err, pod_status_t st, const char* fmt, long long 
   return st;
 }
 
-// MI355X datasheet peaks used only to estimate the prefill share.
+// MI355X datasheet peaks used only to estimate the prefill share, with the
+// fractions of them the kernels reach (measured: prefill 0.4-1 PFLOP/s,
+// decode 5-6.4 TB/s).
 constexpr double kPeakFlops = 2.5e15;   // dense bf16 MFMA, FLOP/s
 constexpr double kPeakBytes = 8.0e12;   // HBM3E, B/s
-constexpr double kPrefillEff = 0.35;    // expected fraction of MFMA peak
-constexpr double kDecodeEff = 0.75;     // expected fraction of HBM peak
+constexpr double kPrefillEff = 0.30;    // expected fraction of MFMA peak
+constexpr double kDecodeEff = 0.72;     // expected fraction of HBM peak
 
 }  // namespace
 
@@ -96,7 +98,7 @@ pod_status_t validate(const pod_attn_params_t* p, int32_t np, const int32_t* qo,
   return POD_OK;
 }
 
-int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu) {
+int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu, int32_t sched_mode) {
   const auto& p = b.params;
   const int32_t full = 4 * wgs_per_cu;
   if (b.qo.empty()) return 0;
@@ -112,6 +114,10 @@ int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu) {
   const double tp = f / (kPeakFlops * kPrefillEff);
   const double td = by / (kPeakBytes * kDecodeEff);
   int32_t q = (int32_t)std::lround(full * tp / (tp + td));
+  // SPLIT: between 2 and 6 eighths of the CUs start on prefill (decode keeps
+  // HBM busy from half the CUs, and short prefills still need a few CUs to
+  // finish early); COLOCATE: at least one prefill and one decode quarter
+  if (sched_mode == POD_SCHED_SPLIT) return std::min(full - 2, std::max(2, q));
   return std::min(full - 1, std::max(1, q));
 }
 

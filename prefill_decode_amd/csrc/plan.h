@@ -101,7 +101,7 @@ struct Batch {
 struct PlanChoice {
   int32_t wgs_per_cu = 2;
   int32_t prefill_quarters = 4;        // target prefill WGs per CU, in quarters
-  int32_t sched_mode = POD_SCHED_LIVE;
+  int32_t sched_mode = POD_SCHED_SPLIT;   // resolved mode (never AUTO)
 };
 
 // Validation of parameters and lengths; returns POD_OK or an error with text.
@@ -110,8 +110,9 @@ pod_status_t validate(const pod_attn_params_t* p, int32_t np, const int32_t* qo,
                       const pod_attn_tuning_t* t, std::string* err);
 
 // Proportional prefill share ([POD] "The idea"): quarters of a CU's
-// workgroup slots given to prefill, from estimated prefill/decode times.
-int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu);
+// workgroup slots (COLOCATE) or eighths of the CUs (SPLIT) given to prefill,
+// from estimated prefill and decode times.
+int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu, int32_t sched_mode);
 
 // Builds one set of work lists.  `prefill_slots` / `decode_wave_slots` are the
 // concurrent prefill workgroups / decode wavefronts the splits should fill;

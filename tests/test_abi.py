@@ -87,7 +87,7 @@ def test_plan_validation(case, expect):
     (dict(prefill_quarters_per_cu=9), INV), (dict(prefill_quarters_per_cu=-2), INV),
     (dict(prefill_kv_splits=-1), INV), (dict(decode_kv_splits=-1), INV),
     (dict(sched_mode=4), INV), (dict(match_sequential=2), INV),
-    (dict(sched_mode=B.SCHED_TICKET, prefill_quarters_per_cu=8), OK),
+    (dict(sched_mode=B.SCHED_COLOCATE, prefill_quarters_per_cu=8), OK),
 ])
 def test_tuning_validation(tun, expect):
     p = B.make_params(8, 2)

@@ -51,31 +51,52 @@ def test_fullsize_sampled(name):
     torch.cuda.empty_cache()
 
 
-def test_colocation_trace():
-    spec = inputs.config_spec("llama3_8b")
-    say("[trace] llama3_8b")
-    bd = inputs.make_batch_device(spec)
-    runner = B.BatchRunner(bd, B.make_tuning(flags=B.FLAG_TRACE))
+def _trace(spec, bd, mode):
+    runner = B.BatchRunner(bd, B.make_tuning(flags=B.FLAG_TRACE, sched_mode=mode))
     run_path(runner, "fused")
     info = runner.plan.info()
     tr = runner.plan.read_trace()
     n_p, n_d = info["prefill_items"], info["decode_items"]
     assert len(tr) == n_p + n_d
-    role, unit, slot = tr[:, 2], tr[:, 3], tr[:, 1]
+    role, unit = tr[:, 2], tr[:, 3]
     # every unit ran exactly once, in the record of its index
     assert np.array_equal(role, np.r_[np.zeros(n_p), np.ones(n_d)].astype(role.dtype))
     assert np.array_equal(unit, np.r_[np.arange(n_p), np.arange(n_d)].astype(unit.dtype))
     assert np.all(tr[:, 5] >= tr[:, 4])
+    return info, tr
+
+
+def test_scheduler_traces():
+    spec = inputs.config_spec("llama3_8b")
+    say("[trace] llama3_8b")
+    bd = inputs.make_batch_device(spec)
+    # co-location on every CU: most CUs run a prefill and a decode unit at once
+    info, tr = _trace(spec, bd, B.SCHED_COLOCATE)
+    role, slot = tr[:, 2], tr[:, 1]
     both = 0
     slots = np.unique(slot)
     for s in slots:
         m = slot == s
-        p = tr[m & (role == 0)]
-        d = tr[m & (role == 1)]
+        p, d = tr[m & (role == 0)], tr[m & (role == 1)]
         if len(p) and len(d):
             ov = (np.minimum(p[:, 5][:, None], d[:, 5][None, :]) >
                   np.maximum(p[:, 4][:, None], d[:, 4][None, :]))
             both += int(ov.any())
-    say(f"  CUs used {len(slots)}, CUs running prefill and decode at once {both}")
+    say(f"  co-locate: CUs used {len(slots)}, running prefill and decode at once {both}")
     assert len(slots) == 256
     assert both >= 0.5 * len(slots)
+    # CU partition (the default): about q/8 of the CUs start on prefill, and
+    # the prefill and decode units overlap in time across the GPU
+    info, tr = _trace(spec, bd, B.SCHED_AUTO)
+    assert info["sched_mode"] == B.SCHED_SPLIT
+    q = info["prefill_quarters_per_cu"]
+    role, slot, t0, t1 = tr[:, 2], tr[:, 1], tr[:, 4], tr[:, 5]
+    first = {}
+    for i in np.argsort(t0, kind="stable"):
+        first.setdefault(int(slot[i]), int(role[i]))
+    frac = np.mean([r == 0 for r in first.values()])
+    say(f"  split: q {q}, CUs starting on prefill {frac:.3f}")
+    assert len(first) == 256 and abs(frac - q / 8) <= 0.1
+    p_end, d_start = t1[role == 0].max(), t0[role == 1].min()
+    d_end, p_start = t1[role == 1].max(), t0[role == 0].min()
+    assert d_start < p_end and p_start < d_end          # the two parts overlap

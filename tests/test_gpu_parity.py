@@ -95,7 +95,7 @@ def test_fused_equals_matched_sequential_bitwise_and_sched_modes():
     b = inputs.make_batch_host(spec)
     ref = oracle.batch_attention(b)
     results = []
-    for mode in (B.SCHED_LIVE, B.SCHED_TICKET, B.SCHED_ORDERED, B.SCHED_SPLIT):
+    for mode in (B.SCHED_AUTO, B.SCHED_COLOCATE, B.SCHED_ORDERED, B.SCHED_SPLIT):
         for q in (1, 4, 7):
             say(f"[bitwise] mode={mode} quarters={q}")
             t = B.make_tuning(match_sequential=1, sched_mode=mode, prefill_quarters_per_cu=q,

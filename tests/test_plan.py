@@ -210,9 +210,15 @@ def test_small_prefill_regime_accounts_for_colocated_decode():
 def test_proportional_mix():
     q = {n: _spec_lists(inputs.config_spec(n)).info()["prefill_quarters_per_cu"]
          for n in inputs.CONFIG_NAMES}
-    assert q["llama2_7b"] <= 2              # decode-heavy MHA: small prefill share
+    # default (CU partition): 2..6 eighths of the CUs start on prefill
+    assert q["llama2_7b"] == 2              # decode-heavy MHA: smallest prefill share
     assert q["l70b_tp1"] >= 3               # large prefill: about half or more
-    assert 1 <= q["llama3_8b"] <= 7
+    assert all(2 <= q[n] <= 6 for n in q)
+    assert _spec_lists(inputs.config_spec("l70b_tp1"), sched_mode=B.SCHED_SPLIT).info()[
+        "sched_mode"] == B.SCHED_SPLIT
+    assert _spec_lists(inputs.config_spec("l70b_tp1")).info()["sched_mode"] == B.SCHED_SPLIT
+    qc = _spec_lists(inputs.config_spec("llama2_7b"), sched_mode=B.SCHED_COLOCATE).info()
+    assert 1 <= qc["prefill_quarters_per_cu"] <= 7
     only_p = inputs.custom_spec("p", 8, 8, [(256, 512)], [], seed=1)
     only_d = inputs.custom_spec("d", 8, 8, [], [512], seed=1)
     assert _spec_lists(only_p).info()["prefill_quarters_per_cu"] == 8
