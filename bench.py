@@ -332,24 +332,32 @@ def main():
         runner.sequential_run()
     torch.cuda.synchronize()
 
-    ev = [[new_ev() for _ in range(6)] for _ in range(args.steps)]
+    # timed steps: pod_attn_run and pod_attn_sequential_run, each after a
+    # cache-evicting fill, with events only around the whole step
+    ev = [[new_ev() for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
         e = ev[i]
         do_flush(2 * i)
         e[0].record(stream)
-        runner.run_events(e[1], e[2])
-        e[3].record(stream)
+        runner.run()
+        e[1].record(stream)
         do_flush(2 * i + 1)
-        e[4].record(stream)
+        e[2].record(stream)
         runner.sequential_run()
-        e[5].record(stream)
+        e[3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
-    fused_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    seq_ms = np.array([e[4].elapsed_time(e[5]) for e in ev])
+    step_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    seq_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    # the fused kernel alone (events recorded around its launch)
+    kv = [[new_ev() for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        do_flush(i)
+        runner.run_events(kv[i][0], kv[i][1])
+    torch.cuda.synchronize()
+    fused_ms = np.array([e[0].elapsed_time(e[1]) for e in kv])
     # warm (no flush) back-to-back
     w0, w1 = new_ev(), new_ev()
     w0.record(stream)

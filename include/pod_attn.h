@@ -108,9 +108,11 @@ typedef struct {
                                     (proportional to the estimated prefill
                                     and decode times, [POD] "The idea") */
   int32_t prefill_kv_splits;     /* 0 = auto; >0 forces this many KV splits per
-                                    prefill tile (capped by its KV tiles) */
+                                    prefill tile (capped by its 64-key tiles and
+                                    by 64) */
   int32_t decode_kv_splits;      /* 0 = auto; >0 forces this many KV splits per
-                                    decode request (capped by its 32-key steps) */
+                                    decode request (capped by its 32-key steps and
+                                    by 64) */
   int32_t match_sequential;      /* 1: sequential_run uses the fused plan's work
                                     lists (for bitwise comparisons) */
   int32_t sched_mode;            /* pod_sched_mode_t */

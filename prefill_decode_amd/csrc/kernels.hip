@@ -975,24 +975,40 @@ __global__ __launch_bounds__(256, 2) void pod_decode_kernel(KernelArgs a) {
   }
 }
 
+// Merge: one wavefront per (row, head).  Lane s reads split s's LSE (all in
+// one load), the wave reduces their max and the weight sum, then the partial
+// O rows (bf16, lane: two of the 128 values) are read -- all loads issued
+// before the weighted sum -- so a task costs two memory round trips whatever
+// its split count.  Splits are summed in index order.
 __global__ __launch_bounds__(256) void pod_merge_kernel(KernelArgs a) {
   const int w = blockIdx.x * kWavesPerWG + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (w >= a.n_m) return;
   const int32_t* t = a.m_tasks + (int64_t)w * M_FIELDS;
   const int out = t[M_OUT], base = t[M_BASE], stride = t[M_STRIDE];
-  const int n = t[M_NFLAG] & 0xFFFF, is_dec = t[M_NFLAG] >> 16;
-  float m = kNegInf;
-  for (int s = 0; s < n; ++s) m = fmax_(m, a.part_lse[base + s * stride]);
-  float acc0 = 0.0f, acc1 = 0.0f, tot = 0.0f;
-  if (m != kNegInf) {
-    for (int s = 0; s < n; ++s) {
-      const int pi = base + s * stride;
-      const float wgt = exp2_(a.part_lse[pi] - m);   // 0 for an empty split
-      const uint32_t v = *(const uint32_t*)(a.part_o + (int64_t)pi * kHeadDim + 2 * lane);
-      acc0 += wgt * __uint_as_float(v << 16);
-      acc1 += wgt * __uint_as_float(v & 0xFFFF0000u);
-      tot += wgt;
+  const int n = t[M_NFLAG] & 0xFFFF, is_dec = t[M_NFLAG] >> 16;   // n <= 64
+  const float ls = lane < n ? a.part_lse[base + lane * stride] : kNegInf;
+  float m = ls;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmax_(m, __shfl_xor(m, off));
+  const float wl = (m == kNegInf || ls == kNegInf) ? 0.0f : exp2_(ls - m);   // 0: empty split
+  float tot = wl;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
+  float acc0 = 0.0f, acc1 = 0.0f;
+  const uint16_t* po = a.part_o + (int64_t)base * kHeadDim + 2 * lane;
+  constexpr int kBatch = 8;
+  for (int s0 = 0; s0 < n; s0 += kBatch) {
+    uint32_t v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      v[i] = s0 + i < n ? *(const uint32_t*)(po + (int64_t)(s0 + i) * stride * kHeadDim) : 0u;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (s0 + i >= n) break;
+      const float wgt = __shfl(wl, s0 + i);
+      acc0 += wgt * __uint_as_float(v[i] << 16);
+      acc1 += wgt * __uint_as_float(v[i] & 0xFFFF0000u);
     }
   }
   const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;

@@ -158,7 +158,7 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
   });
   int32_t s_all = 1;
   if (force_p_splits > 0) {
-    s_all = force_p_splits;
+    s_all = std::min(force_p_splits, kMaxMergeSplits);
   } else if (!tiles.empty()) {
     // [POD] "Cap prefill splitting": at most a few waves of the slots (two
     // for a sequential launch; more for the fused one, whose prefill slots
@@ -233,7 +233,7 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
     const int32_t kv = b.dkv[i];
     const int32_t steps = (int32_t)ceil_div(kv, kDecodeStep);
     int64_t s64 = force_d_splits > 0
-                      ? force_d_splits
+                      ? std::min(force_d_splits, kMaxMergeSplits)
                       : std::min<int64_t>(ceil_div(kv, chunk), kMaxDecodeSplits);
     int32_t s = (int32_t)std::max<int64_t>(1, std::min<int64_t>(s64, steps));
     const int32_t per = (int32_t)ceil_div(steps, s);

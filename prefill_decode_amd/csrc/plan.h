@@ -28,6 +28,7 @@ constexpr int kWavesPerWG = 4;
 constexpr int kMaxXcds = 16;
 constexpr int kMaxPrefillSplits = 16;
 constexpr int kMaxDecodeSplits = 64;
+constexpr int kMaxMergeSplits = 64;     // partials one merge task combines (one per lane)
 constexpr int kMinDecodeChunk = 512;   // keys per decode split, lower bound
 constexpr int kFusedDecodeUnitsPerWave = 2;   // decode units per decode wavefront slot
 constexpr int kSeqDecodeUnitsPerWave = 2;

@@ -238,3 +238,14 @@ def test_decode_items_longest_first_and_pools_by_kv_head():
     for x in range(len(po) - 1):
         kvh = set((P[po[x]:po[x + 1], 1] // g).tolist())
         assert kvh == {x}, (x, kvh)           # 8 KV heads -> one per XCD pool
+
+
+def test_forced_splits_are_capped_at_64():
+    spec = inputs.custom_spec("cap", 8, 2, [(64, 16384)], [16384], seed=5)
+    pl = _spec_lists(spec, prefill_kv_splits=100, decode_kv_splits=100)
+    P = pl.export(0).reshape(-1, P_F)
+    D = pl.export(1).reshape(-1, D_F)
+    assert len(P) == 2 * 64                     # 2 head groups x 1 block x 64 splits
+    assert len(D) == 2 * 64                     # 2 kv heads x 64 splits
+    M = pl.export(2).reshape(-1, M_F)
+    assert int((M[:, 3] & 0xFFFF).max()) == 64
