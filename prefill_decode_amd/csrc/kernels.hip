@@ -538,17 +538,22 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
   const int nsteps = (span + kDecodeStep - 1) / kDecodeStep;
   const int nfull = span / kDecodeStep;
 
-  // Q^T operand: lane holds query j (head h0 + j), d = 32*kk + 8*q4 + e
+  // Q^T operand kk = 2h + p: lane holds query j (head h0 + j), d = 64h +
+  // 16*q4 + 8p + e -- the d order of the K operands below
   u32x4 qf[4];
   {
     const bool ok = j < nq;
-    const uint16_t* qp = a.q_decode + ((int64_t)qi * a.hq + h0 + (ok ? j : 0)) * kHeadDim + 8 * q4;
+    const uint16_t* qp = a.q_decode + ((int64_t)qi * a.hq + h0 + (ok ? j : 0)) * kHeadDim + 16 * q4;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      qf[kk] = ok ? *(const u32x4*)(qp + 32 * kk) : u32x4{0, 0, 0, 0};
+      qf[kk] = ok ? *(const u32x4*)(qp + 64 * (kk >> 1) + 8 * (kk & 1)) : u32x4{0, 0, 0, 0};
   }
 
-  // K operand: key k0 + 16*sb + j, bytes 64*kk + 16*q4   (register 4*sb + kk)
+  // K: a 16-key block sb is fetched as four 1 KB loads, each of eight keys x
+  // one whole 128-byte line (a load of 16 keys x 64 bytes would split every
+  // line over two requests and halve the rate a CU can stream at).  Raw load
+  // 4*sb + 2h + x: lane L reads key 8x + (L & 7), 16-byte chunk 8h + ((L >> 3)
+  // ^ x).  kop() turns the pair x = 0, 1 into MFMA operands of 16 keys x 32 d.
   // V: LDS rows 4i + L/16 (i = 0..7) of the step's slice, chunk L%16.
   // A step's two 16-key blocks each lie in one page (page_size >= 16), so each
   // has one uniform buffer resource; in a unit's last step the blocks and the
@@ -561,24 +566,47 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
     const int64_t rw = addr.block_row(bs);
     return Blk{rsrc(kbase + rw * tok), rsrc(vbase + rw * tok), ke - 1 - bs};
   };
+  const int k8 = lane & 7, kc = lane >> 3;
   auto load_k = [&](int s, u32x4 (&kr)[8]) {
     if (KVM != KV_PAGED_NARROW) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         const Blk bl = block(s, sb);
-        const uint32_t vk = (uint32_t)min(j, bl.rmax) * tok + 16u * q4;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) kr[4 * sb + kk] = bload<kStream>(bl.rk, vk + 64u * kk, 0);
+        for (int x = 0; x < 2; ++x) {
+          const uint32_t vk = (uint32_t)min(8 * x + k8, bl.rmax) * tok + 16u * (kc ^ x);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) kr[4 * sb + 2 * h + x] = bload<kStream>(bl.rk, vk + 128u * h, 0);
+        }
       }
     } else {
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const int tk = min(kb + s * kDecodeStep + 16 * sb + j, ke - 1);
-        const char* pk = kbase + addr.row(tk) * tok + 16 * q4;
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) kr[4 * sb + kk] = gload(pk + 64 * kk);
+        for (int x = 0; x < 2; ++x) {
+          const int tk = min(kb + s * kDecodeStep + 16 * sb + 8 * x + k8, ke - 1);
+          const char* pk = kbase + addr.row(tk) * tok + 16 * (kc ^ x);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) kr[4 * sb + 2 * h + x] = gload(pk + 128 * h);
+        }
+    }
+  };
+  // MFMA operand p of the raw pair (A: x = 0, B: x = 1): lane L gets key
+  // L & 15 and chunk 8h + 2(L >> 4) + p.  p = 0: A in place, lanes 8-15 of
+  // each row from B in place; p = 1: lanes 0-7 take A from 8 lanes up, lanes
+  // 8-15 take B from 8 lanes down (DPP row shifts, bank masks pick the half).
+  auto kop = [](const u32x4& A, const u32x4& B, int p) {
+    u32x4 r;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (p == 0) {
+        r[c] = (uint32_t)__builtin_amdgcn_update_dpp((int)A[c], (int)B[c], 0xE4, 0xF, 0xC, false);
+      } else {
+        const int t = __builtin_amdgcn_update_dpp(0, (int)A[c], 0x108, 0xF, 0x3, false);
+        r[c] = (uint32_t)__builtin_amdgcn_update_dpp(t, (int)B[c], 0x118, 0xF, 0xC, false);
       }
     }
+    return r;
   };
   auto load_v = [&](int s, char* dst) {
     if (KVM != KV_PAGED_NARROW) {
@@ -624,8 +652,11 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
     f32x4 s0 = {}, s1 = {};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(kr[kk]), as_bf(qf[kk]), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(kr[4 + kk]), as_bf(qf[kk]), s1, 0, 0, 0);
+      const int h = kk >> 1, p = kk & 1;
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(kop(kr[2 * h], kr[2 * h + 1], p)),
+                                                   as_bf(qf[kk]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(kop(kr[4 + 2 * h], kr[5 + 2 * h], p)),
+                                                   as_bf(qf[kk]), s1, 0, 0, 0);
     }
     // s0[r]: key k0 + 4*q4 + r; s1[r]: key k0 + 16 + 4*q4 + r; query j
     float x[8];
