@@ -57,13 +57,13 @@ constexpr int kRowBytes = kHeadDim * 2;                      // 256
 constexpr int kTileBytes = kPrefillKeys * kRowBytes;         // 16384
 constexpr int kDecStepBytes = kDecodeStep * kRowBytes;       // 8192
 // A workgroup owns two LDS objects of 32 KiB (64 KiB in all, so two
-// workgroups fit a CU's 160 KiB): X = {K tile 0, V tile 1}, Y = {K tile 1,
-// V tile 0}.  In each prefill iteration the DMAs fill one object while the
-// MFMA operands are read from the other; decode wave w keeps its step buffers
-// of parity 0 / 1 at X + 8w KiB / Y + 8w KiB.  Because the buffers being
-// filled and the buffers being read are distinct objects, the compiler can
-// prove that an LDS DMA in flight does not alias the reads and adds no wait
-// for it.
+// workgroups fit a CU's 160 KiB): X = {K tile 0, V tile 0}, Y = {K tile 1,
+// V tile 1}.  Prefill iteration t reads the tiles of parity t & 1 while the
+// DMAs fill the other parity, so it reads one object and fills the other;
+// decode wave w keeps its step buffers of parity 0 / 1 at X + 8w KiB / Y +
+// 8w KiB.  Because the buffers being filled and the buffers being read are
+// distinct objects, the compiler can prove that an LDS DMA in flight does
+// not alias the reads and adds no wait for it.
 constexpr uint32_t kVSwz = 0xC862EA40u;   // V chunk swizzle by row & 7 (nibble table)
 
 typedef const __attribute__((address_space(4))) int32_t* cptr;   // read-only, scalar-loadable
@@ -889,7 +889,7 @@ __device__ __forceinline__ void trace_unit(const KernelArgs& a, int rec, int rol
   __shared__ int s_info[8];
 
 // prefill tiles: K0, K1, V0, V1
-#define POD_PREFILL_BUFFERS ldsx, ldsy, ldsy + kTileBytes, ldsx + kTileBytes
+#define POD_PREFILL_BUFFERS ldsx, ldsy, ldsx + kTileBytes, ldsy + kTileBytes
 // decode wave w: step buffers of parity 0 / 1
 #define POD_DECODE_BUFFERS(w)                                  \
   char* const db0 = ldsx + (w) * kDecStepBytes;               \
