@@ -339,23 +339,32 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   constexpr float kLazyLog2 = 8.0f;
   float ma = kNegInf, la = 0.0f, mb = kNegInf, lb = 0.0f;
 
-  // S^T of one 32-key half for both blocks: one K operand, two MFMAs
-  auto qk = [&](const char* kb, uint32_t k0, uint32_t kxx, f32x16& sa, f32x16& sb) {
+  // S^T of one 32-key half for both blocks: one K operand, two MFMAs.  The
+  // program order is the issue order: each K operand read one k-step ahead,
+  // and after the first MFMA of every odd k-step one DMA of the next tile
+  // (dma(i), i = 0..3; a no-op in halves that stage nothing), so a DMA that
+  // waits to issue does so while an MFMA runs, and the waves of a CU do not
+  // all issue their DMAs at once.
+  auto qk = [&](const char* kb, uint32_t k0, uint32_t kxx, f32x16& sa, f32x16& sb, auto dma) {
     auto koff = [&](int kk) { return k0 + 32u * ((uint32_t)kk ^ kxx); };
     sa = f32x16{};
     sb = f32x16{};
+    u32x4 kcur = *(const u32x4*)(kb + koff(0));
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const u32x4 kop = *(const u32x4*)(kb + koff(kk));
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kop), as_bf(qa[kk]), sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kop), as_bf(qb[kk]), sb, 0, 0, 0);
+      const u32x4 knext = kk < 7 ? *(const u32x4*)(kb + koff(kk + 1)) : kcur;
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kcur), as_bf(qa[kk]), sa, 0, 0, 0);
+      if (kk & 1) dma(kk >> 1);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kcur), as_bf(qb[kk]), sb, 0, 0, 0);
+      kcur = knext;
     }
-    // K operand reads one k-step ahead of their MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       if (kk < 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (kk & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   };
   // register r holds key key0 + 8 (r >> 2) + (r & 3) (key0 includes 4 hl);
@@ -398,37 +407,46 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
 #pragma unroll
       for (int e = 0; e < 4; ++e) p[ks][e] = pack_bf16x2(sx[8 * ks + 2 * e], sx[8 * ks + 2 * e + 1]);
   };
-  // O^T += V^T P^T for one 32-key half: one V^T operand, two MFMAs
+  // O^T += V^T P^T for one 32-key half: one V^T operand (two transposing
+  // reads), two MFMAs; operand reads one ahead and DMAs placed as in qk
   auto pv = [&](const char* vb, uint32_t v0, uint32_t vxx, const u32x4 (&pa)[2],
-                const u32x4 (&pb)[2]) {
-    auto voff = [&](int db) { return v0 + 64u * ((uint32_t)db ^ vxx); };
+                const u32x4 (&pb)[2], auto dma) {
+    auto vop = [&](int i) {
+      const int ks = i >> 2, db = i & 3;
+      const char* cp = vb + v0 + 64u * ((uint32_t)db ^ vxx) + 16 * ks * kRowBytes;
+      const u32x2 lo = tr_read(cp);
+      const u32x2 hi = tr_read(cp + 8 * kRowBytes);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 vcur = vop(0);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const u32x2 lo = tr_read(vb + voff(db) + 16 * ks * kRowBytes);
-        const u32x2 hi = tr_read(vb + voff(db) + (16 * ks + 8) * kRowBytes);
-        const u32x4 vop = {lo[0], lo[1], hi[0], hi[1]};
-        oa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vop), as_bf(pa[ks]), oa[db], 0, 0, 0);
-        ob[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vop), as_bf(pb[ks]), ob[db], 0, 0, 0);
-      }
-    // V^T operand reads (two per operand) one operand ahead of its MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    for (int i = 0; i < 8; ++i) {
+      const int ks = i >> 2, db = i & 3;
+      const u32x4 vnext = i < 7 ? vop(i + 1) : vcur;
+      oa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vcur), as_bf(pa[ks]), oa[db], 0, 0, 0);
+      if (i & 1) dma(i >> 1);
+      ob[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vcur), as_bf(pb[ks]), ob[db], 0, 0, 0);
+      vcur = vnext;
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   };
   // one 32-key half h of tile t (buffers K kb, V vb).  No instruction is
   // scheduled across a half's boundaries: overlapping two halves would keep
   // both halves' S and operands live, beyond the register file.
-  auto half = [&](int t, int h, const char* kb, const char* vb, bool masked) {
+  auto half = [&](int t, int h, const char* kb, const char* vb, bool masked, auto dma_k,
+                  auto dma_v) {
     __builtin_amdgcn_sched_barrier(0);
     uint32_t k0 = kofs0, kxx = kx, v0 = vofs0, vxx = vx;
     asm volatile("" : "+v"(k0), "+v"(kxx), "+v"(v0), "+v"(vxx));
     f32x16 sa, sb;
-    qk(kb + 32 * h * kRowBytes, k0, kxx, sa, sb);
+    qk(kb + 32 * h * kRowBytes, k0, kxx, sa, sb, dma_k);
     if (masked) {
       const int key0 = kv_begin + t * kPrefillKeys + 32 * h + 4 * hl;
       const int qpos = pos0 + wpos + (threadIdx.x & 31);   // block A's row position
@@ -440,7 +458,7 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
     u32x4 pa[2], pb[2];
     expsum(sa, ma, la, pa);
     expsum(sb, mb, lb, pb);
-    pv(vb + 32 * h * kRowBytes, v0, vxx, pa, pb);
+    pv(vb + 32 * h * kRowBytes, v0, vxx, pa, pb, dma_v);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -449,15 +467,37 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   __amdgpu_buffer_rsrc_t rk = block_rsrc(0, kbase), rv = block_rsrc(0, vbase);
   stage(0, true, 0, rk);
   stage(0, false, 0, rv);
+  // DMA of row group i (rows 4i .. 4i + 3 of this wave's 16) of tile t into
+  // buffers `buf`, without branches (clamped rows), so that it can sit
+  // among a half's MFMAs
+  auto dma_row = [&](int t, bool is_k, int buf, __amdgpu_buffer_rsrc_t r, int i) {
+    int sl = threadIdx.x;
+    asm volatile("" : "+v"(sl));
+    const int dq = (sl >> 4) & 3, dc = sl & 15;
+    char* dst = (is_k ? (buf ? kt1 : kt0) : (buf ? vt1 : vt0)) + wrow;
+    const int rmax = kv_end - 1 - bstart(t);
+    const int rr = 4 * i + dq;
+    const uint32_t vo = (uint32_t)min(rr, rmax) * tok + 16u * (dc ^ (is_k ? kswz(rr) : vswz(rr)));
+    dma16(r, dst + 4 * i * kRowBytes, vo, 0);
+  };
+  auto nothing = [](int) {};
   auto body = [&](int t, auto par) {
     constexpr int P = decltype(par)::value;
     wait_vmem<0>();
     __syncthreads();                       // tile t landed; tile t-1's buffers free
-    if (t + 1 < ntiles) {
-      rk = block_rsrc(t + 1, kbase);
-      rv = block_rsrc(t + 1, vbase);
-      stage(t + 1, true, P ^ 1, rk);
-      stage(t + 1, false, P ^ 1, rv);
+    // The next tile goes to the buffers of parity P ^ 1.  With the wide or
+    // contiguous layout its DMAs are spread over the first half's MFMAs; the
+    // last iteration then restages its own tile there (unread, and waited
+    // for before the item ends), which keeps that code free of branches.
+    const bool flat = KVM != KV_PAGED_NARROW && t < t_act;
+    const int tn = flat ? min(t + 1, ntiles - 1) : t + 1;
+    if (tn < ntiles) {
+      rk = block_rsrc(tn, kbase);
+      rv = block_rsrc(tn, vbase);
+      if (!flat) {
+        stage(tn, true, P ^ 1, rk);
+        stage(tn, false, P ^ 1, rv);
+      }
     }
     if (t < t_act) {
       const char* kb = P ? kt1 : kt0;
@@ -469,8 +509,12 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
       // one copy of the half's code (a masked and an unmasked copy would
       // double the live ranges the register allocator has to cover)
       const bool masked = t >= t_mask;
-      half(t, 0, kb, vb, masked);
-      if (h1) half(t, 1, kb, vb, masked);
+      if (KVM != KV_PAGED_NARROW)
+        half(t, 0, kb, vb, masked, [&](int i) { dma_row(tn, true, P ^ 1, rk, i); },
+             [&](int i) { dma_row(tn, false, P ^ 1, rv, i); });
+      else
+        half(t, 0, kb, vb, masked, nothing, nothing);
+      if (h1) half(t, 1, kb, vb, masked, nothing, nothing);
     }
   };
   for (int t = 0; t < ntiles; t += 2) {
@@ -510,6 +554,8 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
       if (hl == 0) a.part_lse[pi] = lse2;
     }
   };
+  // a restaged last tile may still be landing: LDS is reused after the item
+  wait_vmem<0>();
   finish(oa, ma, la, okA, rA);
   finish(ob, mb, lb, okB, rB);
 }
