@@ -446,7 +446,12 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
     uint32_t k0 = kofs0, kxx = kx, v0 = vofs0, vxx = vx;
     asm volatile("" : "+v"(k0), "+v"(kxx), "+v"(v0), "+v"(vxx));
     f32x16 sa, sb;
+    // MFMA phases run at raised wave priority: on a SIMD shared with another
+    // wave in its softmax (VALU) phase, the MFMA issue goes first and the
+    // two waves' phases interleave
+    __builtin_amdgcn_s_setprio(1);
     qk(kb + 32 * h * kRowBytes, k0, kxx, sa, sb, dma_k);
+    __builtin_amdgcn_s_setprio(0);
     if (masked) {
       const int key0 = kv_begin + t * kPrefillKeys + 32 * h + 4 * hl;
       const int qpos = pos0 + wpos + (threadIdx.x & 31);   // block A's row position
@@ -458,7 +463,9 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
     u32x4 pa[2], pb[2];
     expsum(sa, ma, la, pa);
     expsum(sb, mb, lb, pb);
+    __builtin_amdgcn_s_setprio(1);
     pv(vb + 32 * h * kRowBytes, v0, vxx, pa, pb, dma_v);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
