@@ -284,6 +284,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--quarters", type=int, default=-1, help="prefill quarters per CU (-1 auto)")
+    ap.add_argument("--prefill-splits", type=int, default=0, help="force prefill KV splits (0 auto)")
+    ap.add_argument("--decode-splits", type=int, default=0, help="force decode KV splits (0 auto)")
     ap.add_argument("--sched", type=int, default=0,
                     help="0 auto, 1 co-locate on every CU, 2 ordered, 3 CU partition")
     ap.add_argument("--pmc-run", action="store_true")
@@ -311,7 +313,8 @@ def main():
     spec = inputs.config_spec(args.config, n_dec=args.n_dec)
     batch = inputs.make_batch_device(spec)
     counts = metrics.algorithmic_counts(spec)
-    tuning = B.make_tuning(prefill_quarters_per_cu=args.quarters, sched_mode=args.sched)
+    tuning = B.make_tuning(prefill_quarters_per_cu=args.quarters, sched_mode=args.sched,
+                           prefill_kv_splits=args.prefill_splits, decode_kv_splits=args.decode_splits)
     t0 = time.perf_counter()
     runner = B.BatchRunner(batch, tuning)
     torch.cuda.synchronize()

@@ -94,7 +94,7 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   // Sequential plan: each kernel has the whole GPU.
   pl->seq_is_fused = t.match_sequential == 1;
   if (!pl->seq_is_fused)
-    build_lists(pl->batch, dev, slots, 2, slots * kWavesPerWG, kSeqDecodeUnitsPerWave,
+    build_lists(pl->batch, dev, slots, kSeqPrefillItemsPerSlot, slots * kWavesPerWG, kSeqDecodeUnitsPerWave,
                 t.prefill_kv_splits, t.decode_kv_splits, &pl->seq);
   const WorkLists& sq = pl->seq_is_fused ? pl->fused : pl->seq;
   pl->n_partials = std::max(pl->fused.n_partials, sq.n_partials);
@@ -372,7 +372,7 @@ pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t
   if (after_fused && (e = hipEventRecord(after_fused, stream)) != hipSuccess)
     return hip_err(e, "hipEventRecord(after_fused)");
   if (w.n_m() > 0) {
-    e = launch_merge(a, (w.n_m() + kWavesPerWG - 1) / kWavesPerWG, stream);
+    e = launch_merge(a, (w.n_m() + kMergeTasksPerWG - 1) / kMergeTasksPerWG, stream);
     if (e != hipSuccess) return hip_err(e, "merge kernel launch");
   }
   return POD_OK;
@@ -404,7 +404,7 @@ pod_status_t pod_attn_sequential_run(pod_attn_plan_t pl, const pod_attn_tensors_
     if (e != hipSuccess) return hip_err(e, "decode kernel launch");
   }
   if (w.n_m() > 0) {
-    hipError_t e = launch_merge(a, (w.n_m() + kWavesPerWG - 1) / kWavesPerWG, stream);
+    hipError_t e = launch_merge(a, (w.n_m() + kMergeTasksPerWG - 1) / kMergeTasksPerWG, stream);
     if (e != hipSuccess) return hip_err(e, "merge kernel launch");
   }
   return POD_OK;

@@ -14,18 +14,20 @@
 //     style) whose partials are merged by log-sum-exp ([PAT] abstract).
 //
 // Design for gfx950 (not a translation of the pages' CUDA kernels):
-//   prefill  128 query rows x 1 head per workgroup (4 waves x 32 rows), keys
-//            in tiles of 64 staged through LDS (double buffered; V stored
-//            transposed), S^T = K Q^T and O^T += V^T P^T on
-//            v_mfma_f32_32x32x16_bf16 so that each lane owns one query row:
-//            the softmax state is lane-local and P feeds the next MFMA
-//            straight from the accumulator registers.
+//   prefill  256 (position, head) rows per workgroup: up to 4 query heads of
+//            one KV head x 256/heads positions, 64 rows per wave as two
+//            32-row MFMA blocks; keys in 64-key tiles staged by LDS DMA
+//            (double buffered, XOR-swizzled rows), S^T = K Q^T and O^T +=
+//            V^T P^T on v_mfma_f32_32x32x16_bf16 so that each lane owns one
+//            query row: the softmax state is lane-local and P feeds the next
+//            MFMA straight from the accumulator registers.
 //   decode   one wavefront = one unit (request, KV head, <=16 query heads,
-//            KV split); K is loaded from HBM directly in MFMA operand layout
-//            (16-byte loads), V is loaded as full 256-byte rows and transposed
-//            through a per-wave LDS slice; 16x16x32 MFMAs; loads of step i+1
-//            are in flight while step i computes.
-//   merge    one wavefront per (row, head): log-sum-exp of split partials.
+//            KV split); K is loaded from HBM as whole 128-byte lines into
+//            registers and rearranged into MFMA operands by DPP row shifts,
+//            V goes by LDS DMA into a per-wave slice and is read back
+//            transposed; 16x16x32 MFMAs; loads of step i+1 are in flight
+//            while step i computes.
+//   merge    one 16-lane group per (row, head): log-sum-exp of split partials.
 // All softmax arithmetic is fp32 in the log2 domain (scores scaled by
 // sm_scale*log2(e), exp2); LSE is converted to natural log on output.
 
@@ -1059,47 +1061,77 @@ __global__ __launch_bounds__(256, 2) void pod_decode_kernel(KernelArgs a) {
   }
 }
 
-// Merge: one wavefront per (row, head).  Lane s reads split s's LSE (all in
-// one load), the wave reduces their max and the weight sum, then the partial
-// O rows (bf16, lane: two of the 128 values) are read -- all loads issued
-// before the weighted sum -- so a task costs two memory round trips whatever
-// its split count.  Splits are summed in index order.
+// Merge: one 16-lane group per (row, head) task, four tasks per wavefront.
+// Every load of a task -- its split LSEs (lane j holds splits j, j + 16, ..)
+// and its bf16 partial rows (16 lanes x 16 bytes = one row) -- is issued
+// before any arithmetic, so a task costs about one memory round trip.
+// Splits are summed in index order.
 __global__ __launch_bounds__(256) void pod_merge_kernel(KernelArgs a) {
-  const int w = blockIdx.x * kWavesPerWG + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (w >= a.n_m) return;
-  const int32_t* t = a.m_tasks + (int64_t)w * M_FIELDS;
-  const int out = t[M_OUT], base = t[M_BASE], stride = t[M_STRIDE];
-  const int n = t[M_NFLAG] & 0xFFFF, is_dec = t[M_NFLAG] >> 16;   // n <= 64
-  const float ls = lane < n ? a.part_lse[base + lane * stride] : kNegInf;
-  float m = ls;
+  const int g = lane >> 4, j = lane & 15;
+  const int task = blockIdx.x * kMergeTasksPerWG + (threadIdx.x >> 6) * 4 + g;
+  const bool live = task < a.n_m;
+  const u32x4 tf = *(const u32x4*)(a.m_tasks + (int64_t)(live ? task : 0) * M_FIELDS);
+  const int out = (int)tf[M_OUT], base = (int)tf[M_BASE], stride = (int)tf[M_STRIDE];
+  const int n = live ? (int)(tf[M_NFLAG] & 0xFFFFu) : 0;      // n <= 64
+  const bool is_dec = (tf[M_NFLAG] >> 16) != 0;
+  float ls[4];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmax_(m, __shfl_xor(m, off));
-  const float wl = (m == kNegInf || ls == kNegInf) ? 0.0f : exp2_(ls - m);   // 0: empty split
-  float tot = wl;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
-  float acc0 = 0.0f, acc1 = 0.0f;
-  const uint16_t* po = a.part_o + (int64_t)base * kHeadDim + 2 * lane;
+  for (int c = 0; c < 4; ++c)
+    ls[c] = 16 * c + j < n ? a.part_lse[base + (16 * c + j) * stride] : kNegInf;
   constexpr int kBatch = 8;
-  for (int s0 = 0; s0 < n; s0 += kBatch) {
-    uint32_t v[kBatch];
+  const uint16_t* po = a.part_o + (int64_t)base * kHeadDim + 8 * j;
+  u32x4 v[kBatch];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i)
-      v[i] = s0 + i < n ? *(const uint32_t*)(po + (int64_t)(s0 + i) * stride * kHeadDim) : 0u;
+  for (int i = 0; i < kBatch; ++i)
+    v[i] = i < n ? *(const u32x4*)(po + (int64_t)i * stride * kHeadDim) : u32x4{0, 0, 0, 0};
+  // max and weight sum over the group's 16 lanes
+  float m = fmax_(fmax_(ls[0], ls[1]), fmax_(ls[2], ls[3]));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) m = fmax_(m, __shfl_xor(m, off));
+  float wl[4], tot = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    wl[c] = (m == kNegInf || ls[c] == kNegInf) ? 0.0f : exp2_(ls[c] - m);   // 0: empty split
+    tot += wl[c];
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
+  // the loop runs to the largest n of the wave's four tasks
+  int nmax = n;
+  nmax = max(nmax, __shfl_xor(nmax, 16));
+  nmax = max(nmax, __shfl_xor(nmax, 32));
+  nmax = rfl(nmax);
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int s0 = 0; s0 < nmax; s0 += kBatch) {
+    if (s0 > 0) {
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        v[i] = s0 + i < n ? *(const u32x4*)(po + (int64_t)(s0 + i) * stride * kHeadDim)
+                          : u32x4{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      if (s0 + i >= n) break;
-      const float wgt = __shfl(wl, s0 + i);
-      acc0 += wgt * __uint_as_float(v[i] << 16);
-      acc1 += wgt * __uint_as_float(v[i] & 0xFFFF0000u);
+      const int sp = s0 + i;                                   // uniform
+      if (sp >= nmax) break;
+      const float wsrc = sp < 16 ? wl[0] : sp < 32 ? wl[1] : sp < 48 ? wl[2] : wl[3];
+      const float wgt = sp < n ? __shfl(wsrc, 16 * g + (sp & 15)) : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += wgt * __uint_as_float(v[i][e] << 16);
+        acc[2 * e + 1] += wgt * __uint_as_float(v[i][e] & 0xFFFF0000u);
+      }
     }
   }
+  if (!live) return;
   const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
-  uint16_t* o = (is_dec ? a.o_decode : a.o_prefill) + (int64_t)out * kHeadDim + 2 * lane;
-  *(uint32_t*)o = pack_bf16x2(acc0 * inv, acc1 * inv);
+  uint16_t* o = (is_dec ? a.o_decode : a.o_prefill) + (int64_t)out * kHeadDim + 8 * j;
+  *(u32x4*)o = u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                     pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
   float* lse = is_dec ? a.lse_decode : a.lse_prefill;
-  if (lane == 0 && lse) lse[out] = tot > 0.0f ? (m + log2_(tot)) * kLn2 : kNegInf;
+  if (j == 0 && lse) lse[out] = tot > 0.0f ? (m + log2_(tot)) * kLn2 : kNegInf;
 }
 
 __global__ void pod_probe_kernel(int32_t* out) {

@@ -28,12 +28,16 @@ constexpr int kWavesPerWG = 4;
 constexpr int kMaxXcds = 16;
 constexpr int kMaxPrefillSplits = 16;
 constexpr int kMaxDecodeSplits = 64;
-constexpr int kMaxMergeSplits = 64;     // partials one merge task combines (one per lane)
+constexpr int kMaxMergeSplits = 64;     // partials one merge task combines
+constexpr int kMergeTasksPerWG = 16;    // merge: 4 tasks per wavefront (16 lanes each)
 constexpr int kMinDecodeChunk = 512;   // keys per decode split, lower bound
 constexpr int kFusedDecodeUnitsPerWave = 2;   // decode units per decode wavefront slot
 constexpr int kSeqDecodeUnitsPerWave = 2;
-constexpr int kFusedPrefillItemsPerSlot = 4;  // fused: prefill KV splits aim at this many
-                                              // items per prefill slot (shorter tail)
+// prefill KV splits aim at this many items per prefill slot: more items
+// shorten the tail, fewer write and merge fewer partials (measured on the
+// llama3-8b layer: 2 per slot in the fused plan, 1 in the sequential one)
+constexpr int kFusedPrefillItemsPerSlot = 2;
+constexpr int kSeqPrefillItemsPerSlot = 1;
 
 // Prefill work item (8 int32).
 enum PItem : int {
