@@ -210,10 +210,10 @@ def test_small_prefill_regime_accounts_for_colocated_decode():
 def test_proportional_mix():
     q = {n: _spec_lists(inputs.config_spec(n)).info()["prefill_quarters_per_cu"]
          for n in inputs.CONFIG_NAMES}
-    # default (CU partition): 2..6 eighths of the CUs start on prefill
-    assert q["llama2_7b"] == 2              # decode-heavy MHA: smallest prefill share
+    # default (CU partition): 3..6 eighths of the CUs start on prefill
+    assert q["llama2_7b"] == 3              # decode-heavy MHA: smallest prefill share
     assert q["l70b_tp1"] >= 3               # large prefill: about half or more
-    assert all(2 <= q[n] <= 6 for n in q)
+    assert all(3 <= q[n] <= 6 for n in q)
     assert _spec_lists(inputs.config_spec("l70b_tp1"), sched_mode=B.SCHED_SPLIT).info()[
         "sched_mode"] == B.SCHED_SPLIT
     assert _spec_lists(inputs.config_spec("l70b_tp1")).info()["sched_mode"] == B.SCHED_SPLIT
