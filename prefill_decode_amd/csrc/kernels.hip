@@ -837,17 +837,24 @@ __device__ __forceinline__ int peek(int* c) {
   return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Prefill claim (one thread): the pool of this XCD first, then the others.
-// The pools' counters are read together first (one round trip), then an
-// atomic is spent only on a pool that still had items.
+// Prefill claim (one thread): one atomic on the pool of this XCD; only when
+// that pool is empty are the other pools' counters read together (one round
+// trip) and an atomic spent on one that still had items.  Under decode
+// traffic a round trip costs microseconds, so the common case takes one.
 __device__ __forceinline__ int claim_prefill(const KernelArgs& a, int xcc) {
   const int np = a.num_pools;
+  {
+    const int p = xcc % np;
+    const int n = a.pool_off[p + 1] - a.pool_off[p];
+    const int k = atomicAdd(hot(a, CS_POOL + p), 1);
+    if (k < n) return a.pool_off[p] + k;
+  }
   int seen[kMaxPools];
 #pragma unroll
-  for (int i = 0; i < kMaxPools; ++i)
+  for (int i = 1; i < kMaxPools; ++i)
     seen[i] = i < np ? peek(hot(a, CS_POOL + (xcc + i) % np)) : 0;
 #pragma unroll
-  for (int i = 0; i < kMaxPools; ++i) {
+  for (int i = 1; i < kMaxPools; ++i) {
     if (i >= np) break;
     const int p = (xcc + i) % np;
     const int n = a.pool_off[p + 1] - a.pool_off[p];
@@ -861,19 +868,24 @@ __device__ __forceinline__ int claim_prefill(const KernelArgs& a, int xcc) {
 // Decode claim (one thread, for its workgroup): a group of kWavesPerWG
 // consecutive units of the longest-first list, one per wave.  Groups are
 // dealt round-robin to n_dq queues (queue q: groups q, q + n_dq, ..), so every
-// queue is balanced and longest first too; the caller's own queue q0 is
-// tried first.  The queues' counters are read together first (one round trip).
+// queue is balanced and longest first too.  One atomic on the caller's own
+// queue q0; only when it is empty are the other queues' counters read
+// together and an atomic spent on one that still had groups.
 // A workgroup's four waves start and end their units together, as in a grid
 // launch of one group per workgroup, which measured faster than units taken
 // one wave at a time (those keep every wave streaming to the very end).
 __device__ __forceinline__ int claim_decode_group(const KernelArgs& a, int q0) {
   const int nq = a.n_dq, ng = a.n_groups;
+  {
+    const int g = q0 + nq * atomicAdd(hot(a, CS_DQ + q0), 1);
+    if (g < ng) return g;
+  }
   int seen[kMaxDecodeQueues];
 #pragma unroll
-  for (int i = 0; i < kMaxDecodeQueues; ++i)
+  for (int i = 1; i < kMaxDecodeQueues; ++i)
     seen[i] = i < nq ? peek(hot(a, CS_DQ + (q0 + i) % nq)) : ng;
 #pragma unroll
-  for (int i = 0; i < kMaxDecodeQueues; ++i) {
+  for (int i = 1; i < kMaxDecodeQueues; ++i) {
     if (i >= nq) break;
     const int q = (q0 + i) % nq;
     if (q + nq * seen[i] >= ng) continue;
