@@ -27,7 +27,8 @@ constexpr int CS_POOL = 0;                 // +pool: claims from prefill pool (<
 constexpr int CS_DQ = 16;                  // +queue: claims from decode queue (< kMaxDecodeQueues)
 constexpr int CS_DONE = 48;                // +g (8 groups by blockIdx % 8): finished WGs
 constexpr int CS_DONE_ALL = 56;            // groups whose WGs all finished
-constexpr int kCtrSlots = 57;
+constexpr int CS_EMPTY = 57;               // +role (0 prefill, 1 decode): every queue of the role was seen empty
+constexpr int kCtrSlots = 59;
 constexpr int kCuCounters = 2048;          // per-CU role counters (fused kernel), one per
 constexpr int kCellStride = 16;            // 64-byte line each
 constexpr int kCuCounterOff = kCtrSlots * kCtrStride;

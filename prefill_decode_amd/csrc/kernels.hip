@@ -837,22 +837,26 @@ __device__ __forceinline__ int peek(int* c) {
   return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Prefill claim (one thread): one atomic on the pool of this XCD; only when
-// that pool is empty are the other pools' counters read together (one round
-// trip) and an atomic spent on one that still had items.  Under decode
-// traffic a round trip costs microseconds, so the common case takes one.
-__device__ __forceinline__ int claim_prefill(const KernelArgs& a, int xcc) {
+// Claims (one thread, for its workgroup).  A claim issues, all at once, the
+// atomic on the caller's own pool or queue, reads of the other pools' or
+// queues' counters, and a read of the other role's "empty" flag, so that it
+// costs one round trip (microseconds under decode traffic) whether or not
+// the caller's own queue still has work.  Only when the own queue is empty
+// is an atomic spent on another one that still had work.  A caller that sees
+// every queue of its role empty sets that role's flag and learns from
+// *other_empty whether the other role was empty too (then it can exit).
+//
+// Prefill: one item per claim from the per-XCD pools (pool xcc first).
+__device__ __forceinline__ int claim_prefill(const KernelArgs& a, int xcc, int* other_empty) {
   const int np = a.num_pools;
-  {
-    const int p = xcc % np;
-    const int n = a.pool_off[p + 1] - a.pool_off[p];
-    const int k = atomicAdd(hot(a, CS_POOL + p), 1);
-    if (k < n) return a.pool_off[p] + k;
-  }
+  const int p0 = xcc % np;
+  const int k0 = atomicAdd(hot(a, CS_POOL + p0), 1);
   int seen[kMaxPools];
 #pragma unroll
   for (int i = 1; i < kMaxPools; ++i)
     seen[i] = i < np ? peek(hot(a, CS_POOL + (xcc + i) % np)) : 0;
+  const int oe = peek(hot(a, CS_EMPTY + 1));
+  if (k0 < a.pool_off[p0 + 1] - a.pool_off[p0]) return a.pool_off[p0] + k0;
 #pragma unroll
   for (int i = 1; i < kMaxPools; ++i) {
     if (i >= np) break;
@@ -862,28 +866,27 @@ __device__ __forceinline__ int claim_prefill(const KernelArgs& a, int xcc) {
     const int k = atomicAdd(hot(a, CS_POOL + p), 1);
     if (k < n) return a.pool_off[p] + k;
   }
+  __hip_atomic_store(hot(a, CS_EMPTY + 0), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  *other_empty = oe;
   return -1;
 }
 
-// Decode claim (one thread, for its workgroup): a group of kWavesPerWG
-// consecutive units of the longest-first list, one per wave.  Groups are
-// dealt round-robin to n_dq queues (queue q: groups q, q + n_dq, ..), so every
-// queue is balanced and longest first too.  One atomic on the caller's own
-// queue q0; only when it is empty are the other queues' counters read
-// together and an atomic spent on one that still had groups.
-// A workgroup's four waves start and end their units together, as in a grid
-// launch of one group per workgroup, which measured faster than units taken
-// one wave at a time (those keep every wave streaming to the very end).
-__device__ __forceinline__ int claim_decode_group(const KernelArgs& a, int q0) {
+// Decode: a group of kWavesPerWG consecutive units of the longest-first list,
+// one per wave.  Groups are dealt round-robin to n_dq queues (queue q: groups
+// q, q + n_dq, ..), so every queue is balanced and longest first too; q0 is
+// one of the caller's XCD.  A workgroup's four waves start and end their
+// units together, as in a grid launch of one group per workgroup, which
+// measured faster than units taken one wave at a time (those keep every wave
+// streaming to the very end).
+__device__ __forceinline__ int claim_decode_group(const KernelArgs& a, int q0, int* other_empty) {
   const int nq = a.n_dq, ng = a.n_groups;
-  {
-    const int g = q0 + nq * atomicAdd(hot(a, CS_DQ + q0), 1);
-    if (g < ng) return g;
-  }
+  const int g0 = q0 + nq * atomicAdd(hot(a, CS_DQ + q0), 1);
   int seen[kMaxDecodeQueues];
 #pragma unroll
   for (int i = 1; i < kMaxDecodeQueues; ++i)
     seen[i] = i < nq ? peek(hot(a, CS_DQ + (q0 + i) % nq)) : ng;
+  const int oe = peek(hot(a, CS_EMPTY + 0));
+  if (g0 < ng) return g0;
 #pragma unroll
   for (int i = 1; i < kMaxDecodeQueues; ++i) {
     if (i >= nq) break;
@@ -892,6 +895,8 @@ __device__ __forceinline__ int claim_decode_group(const KernelArgs& a, int q0) {
     const int g = q + nq * atomicAdd(hot(a, CS_DQ + q), 1);
     if (g < ng) return g;
   }
+  __hip_atomic_store(hot(a, CS_EMPTY + 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  *other_empty = oe;
   return -1;
 }
 
@@ -1001,30 +1006,40 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
   // when the claimant is free (greedy list scheduling: the next unit goes to
   // the first worker to finish, which a claim made ahead of time would not
   // honour); a claim costs well under 1% of a unit. ----
-  auto prefill_phase = [&]() {
-    if (a.n_p == 0) return;
+  // Each phase returns whether the other role's queues were all seen empty
+  // when its own ran out (then the workgroup is done).
+  auto prefill_phase = [&]() -> bool {
+    if (a.n_p == 0) return false;
     while (true) {
       __syncthreads();   // the previous unit / phase is done with LDS and s_info
-      if (tid == 0) s_info[2] = claim_prefill(a, xcc);
+      if (tid == 0) {
+        int oe = 0;
+        s_info[2] = claim_prefill(a, xcc, &oe);
+        s_info[3] = oe;
+      }
       __syncthreads();
       const int u = rfl(s_info[2]);
-      if (u < 0) break;
+      if (u < 0) return rfl(s_info[3]) != 0;
       const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
       prefill_tile<KVM>(a, (cptr)a.p_items + u * P_FIELDS, POD_PREFILL_BUFFERS);
       if (a.trace && tid == 0) trace_unit(a, u, 0, u, slot, t0);
     }
   };
   // ---- decode unit groups until the queues are empty: one unit per wave ----
-  auto decode_phase = [&]() {
-    if (a.n_d == 0) return;
+  auto decode_phase = [&]() -> bool {
+    if (a.n_d == 0) return false;
     POD_DECODE_BUFFERS(wave)
     const int q0 = (4 * xcc + (slot & 3)) % a.n_dq;   // one of this XCD's queues
     while (true) {
       __syncthreads();   // the previous group / phase is done with LDS and s_info
-      if (tid == 0) s_info[2] = claim_decode_group(a, q0);
+      if (tid == 0) {
+        int oe = 0;
+        s_info[2] = claim_decode_group(a, q0, &oe);
+        s_info[3] = oe;
+      }
       __syncthreads();
       const int g = rfl(s_info[2]);
-      if (g < 0) break;
+      if (g < 0) return rfl(s_info[3]) != 0;
       const int u = g * kWavesPerWG + wave;
       if (u < a.n_d) {
         const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
@@ -1034,11 +1049,9 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
     }
   };
   if (role0 == 0) {
-    prefill_phase();
-    decode_phase();
+    if (!prefill_phase()) decode_phase();
   } else {
-    decode_phase();
-    prefill_phase();
+    if (!decode_phase()) prefill_phase();
   }
   finish_launch(a, &s_info[4]);
 }
@@ -1047,7 +1060,10 @@ template <int KVM>
 __global__ __launch_bounds__(256, 2) void pod_prefill_kernel(KernelArgs a) {
   POD_LDS_OBJECTS
   zero_next_counters(a);
-  if (threadIdx.x == 0) s_info[0] = claim_prefill(a, cu_slot_id() >> 8);
+  if (threadIdx.x == 0) {
+    int oe;
+    s_info[0] = claim_prefill(a, cu_slot_id() >> 8, &oe);
+  }
   __syncthreads();
   const int unit = s_info[0];
   __syncthreads();
