@@ -217,6 +217,12 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
     }
     while (x < nx) w.pool_off[++x] = (int32_t)pitems.size();
   }
+  // longest first within each pool (a pool shares its K/V whatever the
+  // order): causal row blocks grow with position, and in tile order the
+  // longest items would be claimed last and lengthen the tail
+  for (int32_t x = 0; x < nx; ++x)
+    std::stable_sort(pitems.begin() + w.pool_off[x], pitems.begin() + w.pool_off[x + 1],
+                     [](const PI& a, const PI& c) { return a.work > c.work; });
   for (auto& it : pitems) w.p_items.insert(w.p_items.end(), it.f.begin(), it.f.end());
 
   // ---- decode units (request, KV head, <=16 query heads, split) ----

@@ -226,6 +226,17 @@ def test_proportional_mix():
     assert _spec_lists(only_p, prefill_quarters_per_cu=3).info()["prefill_quarters_per_cu"] == 3
 
 
+def test_prefill_items_longest_first_within_pools():
+    for name in ("llama3_8b", "batched"):
+        pl = _spec_lists(inputs.config_spec(name))
+        P = pl.export(0).reshape(-1, P_F)
+        po = pl.export(6)
+        work = P[:, 2].astype(np.int64) * (P[:, 5] - P[:, 4])
+        for x in range(len(po) - 1):
+            w = work[po[x]:po[x + 1]]
+            assert np.all(np.diff(w) <= 0), (name, x)
+
+
 def test_decode_items_longest_first_and_pools_by_kv_head():
     spec = inputs.config_spec("l70b_tp1")
     pl = _spec_lists(spec)
