@@ -1,6 +1,7 @@
 """GPU parity at the full workload sizes (the launch configuration the bench
-times), checked on sampled rows the oracle computes one by one, plus the
-scheduler's co-location trace on the Llama-3-8B-shaped batch."""
+times): every config on sampled rows the oracle computes one by one and on
+every row against the fp64 oracle of the whole batch, plus the scheduler
+traces on the Llama-3-8B-shaped batch."""
 
 import numpy as np
 import pytest
@@ -48,6 +49,26 @@ def test_fullsize_sampled(name):
         for k in got:
             assert np.all(np.isfinite(got[k])), (name, path, k)
     del runner, bd
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", inputs.CONFIG_NAMES)
+def test_fullsize_every_row(name):
+    # every prefill row and decode of the full-size batch, both paths,
+    # against the fp64 oracle of the whole batch
+    import torch
+    spec = inputs.config_spec(name)
+    say(f"[fullsize-all] {name}: generating on device")
+    bd = inputs.make_batch_device(spec, poison=True)
+    runner = B.BatchRunner(bd)
+    host = inputs.host_subset(bd, list(range(spec.num_prefill)), list(range(spec.num_decode)))
+    say("  oracle on the whole batch")
+    ref = oracle.batch_attention(host)
+    del host
+    for path in ("fused", "seq"):
+        say(f"  path {path}")
+        compare(run_path(runner, path), ref, f"{name}-all/{path}")
+    del runner, bd, ref
     torch.cuda.empty_cache()
 
 
