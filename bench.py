@@ -149,8 +149,9 @@ def cpu_baseline(batch_dev, spec, budget_s=15.0):
 
 
 def pmc_run(args):
-    """Driver for `rocprofv3 --pmc` runs: a few fused runs and one plain 1 GiB
-    device-to-device copy whose counters calibrate the byte counters."""
+    """Driver for `rocprofv3 --pmc` runs: a few fused runs, as many sequential
+    runs, and one plain 1 GiB device-to-device copy whose counters calibrate
+    the byte counters."""
     import torch
 
     from prefill_decode_amd import binding as B
@@ -161,12 +162,15 @@ def pmc_run(args):
     runner = B.BatchRunner(inputs.make_batch_device(spec))
     for _ in range(args.steps):
         runner.run()
+    for _ in range(args.steps):
+        runner.sequential_run()
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    print(f"pmc-run {args.config}: {args.steps} fused runs, one {COPY_BYTES} B copy", flush=True)
+    print(f"pmc-run {args.config}: {args.steps} fused and {args.steps} sequential runs, "
+          f"one {COPY_BYTES} B copy", flush=True)
 
 
 def summarize_pmc(args):
@@ -202,7 +206,8 @@ def summarize_pmc(args):
     txt = f"""# HBM traffic of pod_fused_kernel — {DESCR.get(args.config, args.config)}
 
 Two `rocprofv3 --pmc` passes (one counter each) over `bench.py --pmc-run`:
-{args.steps} fused runs of the batch and one plain {COPY_BYTES}-byte device-to-device copy. The copy's
+{args.steps} fused runs of the batch (then as many sequential runs, not used here) and one plain
+{COPY_BYTES}-byte device-to-device copy. The copy's
 counters calibrate them: bytes per counter unit = {COPY_BYTES} / (the copy's reading).
 
 Commands (from the repository root; `$D` = a scratch directory):
@@ -232,6 +237,61 @@ Commands (from the repository root; `$D` = a scratch directory):
     open(traffic_file(args.config), "w").write(txt)
     print(txt)
     del d
+
+
+COUNTERS = ["MfmaUtil", "LdsBankConflict", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"]
+
+
+def summarize_counters(args):
+    """Reads one `rocprofv3 --pmc` pass of COUNTERS over `--pmc-run` under DIR
+    and writes profiles/counters_<config>.md: MFMA busy share of SIMD cycles
+    and LDS bank conflicts per kernel (means over dispatches)."""
+    import csv
+    from collections import defaultdict
+
+    vals = defaultdict(lambda: defaultdict(list))
+    for f in glob.glob(os.path.join(args.summarize_counters, "**", "*counter_collection.csv"),
+                       recursive=True):
+        for row in csv.DictReader(open(f)):
+            name = row["Kernel_Name"]
+            for k in ("pod_fused_kernel", "pod_prefill_kernel", "pod_decode_kernel",
+                      "pod_merge_kernel"):
+                if k in name:
+                    vals[k][row["Counter_Name"]].append(float(row["Counter_Value"]))
+    if "pod_fused_kernel" not in vals:
+        sys.exit("summarize-counters: no fused-kernel dispatches in the counter CSVs")
+    lines = []
+    for k in ("pod_fused_kernel", "pod_prefill_kernel", "pod_decode_kernel", "pod_merge_kernel"):
+        if k not in vals:
+            continue
+        v = vals[k]
+        mean = lambda c: float(np.mean(v[c])) if v.get(c) else float("nan")
+        lines.append(f"| `{k}` | {len(v.get('MfmaUtil', []))} | {mean('MfmaUtil'):.1f} | "
+                     f"{mean('LdsBankConflict'):.4f} | {mean('SQ_LDS_BANK_CONFLICT'):.4g} | "
+                     f"{mean('SQ_LDS_IDX_ACTIVE'):.4g} |")
+    cnt = " ".join(COUNTERS)
+    txt = f"""# MFMA busy and LDS bank conflicts — {DESCR.get(args.config, args.config)}
+
+One `rocprofv3 --pmc` pass over `bench.py --pmc-run` ({args.steps} fused runs, then {args.steps}
+sequential runs). `MfmaUtil` = MFMA-busy cycles summed over SIMDs / (GPU-active cycles × SIMDs), in
+percent, for the whole launch (idle SIMDs, launch ramp and tail included). `LdsBankConflict` =
+bank-conflict cycles / conflict-free LDS cycles.
+
+Commands (from the repository root; `$D` = a scratch directory):
+
+    cd /tmp && export TMPDIR=/tmp
+    rocprofv3 --pmc {cnt} --output-format csv -d $D -o run -- python3 bench.py --pmc-run --config {args.config} --steps {args.steps}
+    python3 bench.py --summarize-counters $D --config {args.config} --steps {args.steps}
+
+| kernel | dispatches | MfmaUtil % | LdsBankConflict | SQ_LDS_BANK_CONFLICT | SQ_LDS_IDX_ACTIVE |
+|---|---|---|---|---|---|
+""" + "\n".join(lines) + f"""
+
+- sources_sha256: `{sources_digest()}`
+"""
+    os.makedirs(PROFILES, exist_ok=True)
+    open(os.path.join(PROFILES, f"counters_{args.config}.md"), "w").write(txt)
+    print(txt)
 
 
 def summarize_stats(args):
@@ -291,6 +351,7 @@ def main():
     ap.add_argument("--pmc-run", action="store_true")
     ap.add_argument("--summarize-pmc", default=None, metavar="DIR")
     ap.add_argument("--summarize-stats", default=None, metavar="DIR")
+    ap.add_argument("--summarize-counters", default=None, metavar="DIR")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -301,6 +362,8 @@ def main():
         return summarize_pmc(args)
     if args.summarize_stats:
         return summarize_stats(args)
+    if args.summarize_counters:
+        return summarize_counters(args)
     if args.pmc_run:
         return pmc_run(args)
 
