@@ -83,6 +83,11 @@ def lib():
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
                                "`python -m prefill_decode_amd.build` (no fallback exists)")
+        # torch first: its bundled HIP runtime (same soname as the system's)
+        # then serves the library too.  Loaded first, the library would pull
+        # the system runtime in beside torch's, and one of the two would not
+        # see the device.
+        import torch  # noqa: F401
         L = C.CDLL(_LIB_PATH)
         i32p = C.POINTER(C.c_int32)
         L.pod_attn_plan.argtypes = [C.POINTER(Params), C.c_int32, i32p, i32p, C.c_int32, i32p,

@@ -136,3 +136,16 @@ def test_host_plan_cannot_run_and_null_handles():
     # 8 q heads over 2 KV heads: two items of 4 packed heads x 1 position block
     assert info["workspace_bytes"] > 0 and info["prefill_items"] == 2
     pl.destroy()
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    # the library loaded before torch must not bring a second HIP runtime
+    # into the process (one of two would not see the device)
+    import subprocess
+    import sys
+    code = ("import prefill_decode_amd.binding as B\nB.lib()\nimport torch\n"
+            "print(len({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr[-500:]
+    assert r.stdout.strip().splitlines()[-1] == "1", r.stdout
