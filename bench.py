@@ -49,14 +49,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def sources_digest():
-    """sha256 over the library's kernel and planner sources: traffic figures
-    taken from counters are only reported while this matches."""
+    """sha256 over the library's kernel and planner sources and its build
+    script (compile flags change the kernels too): traffic figures taken from
+    counters are only reported while this matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "prefill_decode_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
-        if f.endswith((".hip", ".cpp", ".h")):
-            h.update(os.path.basename(f).encode())
-            h.update(open(f, "rb").read())
+    files = [f for f in sorted(glob.glob(os.path.join(csrc, "*"))) if f.endswith((".hip", ".cpp", ".h"))]
+    for f in files + [os.path.join(ROOT, "prefill_decode_amd", "build.py")]:
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
 
