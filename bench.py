@@ -356,8 +356,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the attention path needs no collectives; DESIGN.md describes how it would "
-              "shard)", file=sys.stderr)
+              "(sharded by KV head or by request, each GPU would run this same kernel on its "
+              "share with no exchange; this library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     if args.summarize_pmc:
         return summarize_pmc(args)
