@@ -114,12 +114,18 @@ int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu, int32_t sched_
   const double tp = f / (kPeakFlops * kPrefillEff);
   const double td = by / (kPeakBytes * kDecodeEff);
   int32_t q = (int32_t)std::lround(full * tp / (tp + td));
-  // SPLIT: between 3 and 6 eighths of the CUs start on prefill.  Below 3 the
-  // prefill runs long beside a decode that cannot use the extra CUs (a CU's
-  // decode rate is capped by its own load issue, and HBM by the sum): measured
-  // on the llama2-7b (decode-heavy) and batched layers, 3 beat 2 by 3-6%.
+  // SPLIT: between 4 and 6 eighths of the CUs start on prefill, 3 when the
+  // estimate puts the prefill under 1/16 of the time.  Fewer prefill CUs make
+  // the prefill run long beside a decode that cannot use the extra CUs (a CU's
+  // decode rate is capped by its own load issue, and HBM by the sum).
+  // Measured: 4 beat 3 by 1-7% on the batched mix at 32-192 decodes and tied
+  // on the llama3-8b layer and at 256 decodes; on the llama2-7b layer (prefill
+  // 4% of the estimate) 3 beat 4 by 2% and 2 by 2-7%.
   // COLOCATE: at least one prefill and one decode quarter.
-  if (sched_mode == POD_SCHED_SPLIT) return std::min(full - 2, std::max(3, q));
+  if (sched_mode == POD_SCHED_SPLIT) {
+    const int32_t lo = 16.0 * tp < tp + td ? 3 : 4;
+    return std::min(full - 2, std::max(lo, q));
+  }
   return std::min(full - 1, std::max(1, q));
 }
 
