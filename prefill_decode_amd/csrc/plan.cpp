@@ -114,16 +114,19 @@ int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu, int32_t sched_
   const double tp = f / (kPeakFlops * kPrefillEff);
   const double td = by / (kPeakBytes * kDecodeEff);
   int32_t q = (int32_t)std::lround(full * tp / (tp + td));
-  // SPLIT: between 4 and 6 eighths of the CUs start on prefill, 3 when the
-  // estimate puts the prefill under 1/16 of the time.  Fewer prefill CUs make
-  // the prefill run long beside a decode that cannot use the extra CUs (a CU's
-  // decode rate is capped by its own load issue, and HBM by the sum).
-  // Measured: 4 beat 3 by 1-7% on the batched mix at 32-192 decodes and tied
-  // on the llama3-8b layer and at 256 decodes; on the llama2-7b layer (prefill
-  // 4% of the estimate) 3 beat 4 by 2% and 2 by 2-7%.
+  // SPLIT: between 3 and 6 eighths of the CUs start on prefill.  Fewer
+  // prefill CUs make the prefill run long beside a decode that cannot use the
+  // extra CUs (a CU's decode rate is capped by its own load issue, and HBM by
+  // the sum): on the llama2-7b layer 3 beat 2 by 2-7%.  With several prefill
+  // requests at least 4 eighths start on prefill (unless the estimate puts
+  // the prefill under 1/16 of the time).  This is fitted to measurements, not
+  // derived: on the batched mix (four prefill requests) 4 beat 3 by 1-7% at
+  // 32-192 decodes and tied at 256, while on the one-request layers the
+  // estimate's own choice held (llama3-8b: 3 stayed 1-2% ahead of 4).
   // COLOCATE: at least one prefill and one decode quarter.
   if (sched_mode == POD_SCHED_SPLIT) {
-    const int32_t lo = 16.0 * tp < tp + td ? 3 : 4;
+    const bool several = b.qo.size() > 1;
+    const int32_t lo = several && 16.0 * tp >= tp + td ? 4 : 3;
     return std::min(full - 2, std::max(lo, q));
   }
   return std::min(full - 1, std::max(1, q));
