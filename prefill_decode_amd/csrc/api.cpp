@@ -82,19 +82,22 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   int64_t sum_qo = 0;
   for (int32_t x : pl->batch.qo) sum_qo += x;
   // Fused plan.  [PR]: with <= 1536 prefill tokens the prefill split count is
-  // sized for the slots left beside the co-located decode workgroups;
-  // otherwise for every slot.
+  // sized for the slots left beside the co-located decode workgroups (and
+  // fewer items per slot); otherwise for every slot.
   const int64_t slots = (int64_t)dev.num_cus * c.wgs_per_cu;
   const int64_t p_slots_coloc = std::max<int64_t>(1, (int64_t)dev.num_cus * c.prefill_quarters / 4);
-  const int64_t fused_p_slots = sum_qo <= 1536 ? p_slots_coloc : slots;
+  const bool small_prefill = sum_qo <= 1536;
+  const int64_t fused_p_slots = small_prefill ? p_slots_coloc : slots;
   const int64_t fused_d_waves =
       std::max<int64_t>(kWavesPerWG, (int64_t)dev.num_cus * (4 * c.wgs_per_cu - c.prefill_quarters));
-  build_lists(pl->batch, dev, fused_p_slots, kFusedPrefillItemsPerSlot, fused_d_waves,
-              kFusedDecodeUnitsPerWave, t.prefill_kv_splits, t.decode_kv_splits, &pl->fused);
+  const int32_t p_half_items =
+      small_prefill ? kFusedPrefillHalfItemsPerSlotSmall : kFusedPrefillHalfItemsPerSlotLarge;
+  build_lists(pl->batch, dev, fused_p_slots, p_half_items, fused_d_waves, kFusedDecodeUnitsPerWave,
+              t.prefill_kv_splits, t.decode_kv_splits, &pl->fused);
   // Sequential plan: each kernel has the whole GPU.
   pl->seq_is_fused = t.match_sequential == 1;
   if (!pl->seq_is_fused)
-    build_lists(pl->batch, dev, slots, kSeqPrefillItemsPerSlot, slots * kWavesPerWG, kSeqDecodeUnitsPerWave,
+    build_lists(pl->batch, dev, slots, kSeqPrefillHalfItemsPerSlot, slots * kWavesPerWG, kSeqDecodeUnitsPerWave,
                 t.prefill_kv_splits, t.decode_kv_splits, &pl->seq);
   const WorkLists& sq = pl->seq_is_fused ? pl->fused : pl->seq;
   pl->n_partials = std::max(pl->fused.n_partials, sq.n_partials);

@@ -133,7 +133,7 @@ int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu, int32_t sched_
 }
 
 void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_slots,
-                 int32_t p_items_per_slot, int64_t decode_wave_slots, int32_t d_units_per_slot,
+                 int32_t p_half_items_per_slot, int64_t decode_wave_slots, int32_t d_units_per_slot,
                  int32_t force_p_splits, int32_t force_d_splits, WorkLists* out) {
   const auto& p = b.params;
   const int32_t hq = p.num_qo_heads, hkv = p.num_kv_heads, g = hq / hkv;
@@ -171,11 +171,10 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
   if (force_p_splits > 0) {
     s_all = std::min(force_p_splits, kMaxMergeSplits);
   } else if (!tiles.empty()) {
-    // [POD] "Cap prefill splitting": at most a few waves of the slots (two
-    // for a sequential launch; more for the fused one, whose prefill slots
-    // run beside decode and whose last items form its tail).
+    // [POD] "Cap prefill splitting": a few waves of items over the slots at
+    // most (the caller's count per slot; one for a sequential launch).
     s_all = (int32_t)std::max<int64_t>(
-        1, (std::max(1, p_items_per_slot) * prefill_slots) / (int64_t)tiles.size());
+        1, (std::max(1, p_half_items_per_slot) * prefill_slots) / (2 * (int64_t)tiles.size()));
     s_all = std::min(s_all, kMaxPrefillSplits);
   }
   struct PI { std::vector<int32_t> f; double work; };
