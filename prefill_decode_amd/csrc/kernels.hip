@@ -574,10 +574,14 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
 // 32 keys per step.  K goes straight from HBM into MFMA operand registers; V
 // goes by LDS DMA into the wave's double-buffered slice and is read back
 // transposed.  The loads of step s+1 are in flight while step s computes.
+// With `ahead` set, lane 0 takes a ticket of that queue counter in the
+// unit's second-to-last step, right after the last V DMA (so the last step's
+// wait for its V covers the ticket too) and returns it in `ticket`; the
+// caller's next claim then costs no round trip of its own.
 // ---------------------------------------------------------------------------
 template <int KVM>
 __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* __restrict__ vb0,
-                                            char* __restrict__ vb1) {
+                                            char* __restrict__ vb1, int* ahead, int& ticket) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, q4 = lane >> 4;
   const int qi = it[D_QROW], h0 = it[D_HEAD0], nq = it[D_NQ];
@@ -764,6 +768,7 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
     }
     lds_fence();
     if (more) load_v(s + 1, vnext);
+    if (ahead != nullptr && s == nsteps - 2 && lane == 0) ticket = atomicAdd(ahead, 1);
 #pragma unroll
     for (int db = 0; db < 8; ++db)
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(af[db]), as_bf(pb), o[db], 0, 0, 0);
@@ -874,19 +879,16 @@ __device__ __forceinline__ int claim_prefill(const KernelArgs& a, int xcc, int* 
 // Decode: a group of kWavesPerWG consecutive units of the longest-first list,
 // one per wave.  Groups are dealt round-robin to n_dq queues (queue q: groups
 // q, q + n_dq, ..), so every queue is balanced and longest first too; q0 is
-// one of the caller's XCD.  A workgroup's four waves start and end their
-// units together, as in a grid launch of one group per workgroup, which
-// measured faster than units taken one wave at a time (those keep every wave
+// one of the caller's XCD.  A workgroup's four waves start their units
+// together, as in a grid launch of one group per workgroup, which measured
+// faster than units taken one wave at a time (those keep every wave
 // streaming to the very end).
-__device__ __forceinline__ int claim_decode_group(const KernelArgs& a, int q0, int* other_empty) {
+//
+// The own queue is empty: claim from the others (seen[i]: the counter of
+// queue q0 + i as read earlier), else mark the role empty.
+__device__ __forceinline__ int claim_decode_others(const KernelArgs& a, int q0, const int* seen,
+                                                   int oe, int* other_empty) {
   const int nq = a.n_dq, ng = a.n_groups;
-  const int g0 = q0 + nq * atomicAdd(hot(a, CS_DQ + q0), 1);
-  int seen[kMaxDecodeQueues];
-#pragma unroll
-  for (int i = 1; i < kMaxDecodeQueues; ++i)
-    seen[i] = i < nq ? peek(hot(a, CS_DQ + (q0 + i) % nq)) : ng;
-  const int oe = peek(hot(a, CS_EMPTY + 0));
-  if (g0 < ng) return g0;
 #pragma unroll
   for (int i = 1; i < kMaxDecodeQueues; ++i) {
     if (i >= nq) break;
@@ -898,6 +900,33 @@ __device__ __forceinline__ int claim_decode_group(const KernelArgs& a, int q0, i
   __hip_atomic_store(hot(a, CS_EMPTY + 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   *other_empty = oe;
   return -1;
+}
+
+__device__ __forceinline__ int claim_decode_group(const KernelArgs& a, int q0, int* other_empty) {
+  const int nq = a.n_dq, ng = a.n_groups;
+  const int g0 = q0 + nq * atomicAdd(hot(a, CS_DQ + q0), 1);
+  int seen[kMaxDecodeQueues];
+#pragma unroll
+  for (int i = 1; i < kMaxDecodeQueues; ++i)
+    seen[i] = i < nq ? peek(hot(a, CS_DQ + (q0 + i) % nq)) : ng;
+  const int oe = peek(hot(a, CS_EMPTY + 0));
+  if (g0 < ng) return g0;
+  return claim_decode_others(a, q0, seen, oe, other_empty);
+}
+
+// The same claim with the own queue's ticket already taken (decode_unit's
+// `ahead`): no round trip while that queue has work.
+__device__ __forceinline__ int claim_decode_after(const KernelArgs& a, int q0, int ticket,
+                                                  int* other_empty) {
+  const int nq = a.n_dq, ng = a.n_groups;
+  const int g0 = q0 + nq * ticket;
+  if (g0 < ng) return g0;
+  int seen[kMaxDecodeQueues];
+#pragma unroll
+  for (int i = 1; i < kMaxDecodeQueues; ++i)
+    seen[i] = i < nq ? peek(hot(a, CS_DQ + (q0 + i) % nq)) : ng;
+  const int oe = peek(hot(a, CS_EMPTY + 0));
+  return claim_decode_others(a, q0, seen, oe, other_empty);
 }
 
 // First workgroup of a launch: zero the counter block of the next launch of
@@ -1025,26 +1054,42 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
       if (a.trace && tid == 0) trace_unit(a, u, 0, u, slot, t0);
     }
   };
-  // ---- decode unit groups until the queues are empty: one unit per wave ----
+  // ---- decode unit groups until the queues are empty: one unit per wave.
+  // Wave 0 claims the next group as soon as its own unit is done, with the
+  // ticket it took a step before that unit's end (a claim made at the end
+  // costs a memory round trip, microseconds under decode traffic, in which
+  // the four waves would idle; held for about a step, the claimed group
+  // upsets no balance).  The claim goes to the s_info pair the current group
+  // did not read, so the other waves may still be reading theirs. ----
   auto decode_phase = [&]() -> bool {
     if (a.n_d == 0) return false;
     POD_DECODE_BUFFERS(wave)
     const int q0 = (4 * xcc + (slot & 3)) % a.n_dq;   // one of this XCD's queues
+    __syncthreads();   // the previous phase is done with LDS and s_info
+    if (tid == 0) {
+      int oe = 0;
+      s_info[2] = claim_decode_group(a, q0, &oe);
+      s_info[3] = oe;
+    }
+    int pair = 2;   // s_info pair holding the current claim: 2 or 5
     while (true) {
-      __syncthreads();   // the previous group / phase is done with LDS and s_info
-      if (tid == 0) {
-        int oe = 0;
-        s_info[2] = claim_decode_group(a, q0, &oe);
-        s_info[3] = oe;
-      }
-      __syncthreads();
-      const int g = rfl(s_info[2]);
-      if (g < 0) return rfl(s_info[3]) != 0;
-      const int u = g * kWavesPerWG + wave;
+      __syncthreads();   // the claim is visible
+      const int g = rfl(s_info[pair]);
+      if (g < 0) return rfl(s_info[pair + 1]) != 0;
+      const int u = g * kWavesPerWG + wave;   // wave 0's unit always exists
+      int ticket = -1;
       if (u < a.n_d) {
         const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
-        decode_unit<KVM>(a, (cptr)a.d_items + u * D_FIELDS, db0, db1);
+        decode_unit<KVM>(a, (cptr)a.d_items + u * D_FIELDS, db0, db1,
+                         wave == 0 ? hot(a, CS_DQ + q0) : nullptr, ticket);
         if (a.trace && lane == 0) trace_unit(a, a.n_p + u, 1, u, slot, t0);
+      }
+      pair = 7 - pair;
+      if (tid == 0) {
+        int oe = 0;
+        s_info[pair] = ticket >= 0 ? claim_decode_after(a, q0, ticket, &oe)
+                                   : claim_decode_group(a, q0, &oe);
+        s_info[pair + 1] = oe;
       }
     }
   };
@@ -1084,7 +1129,8 @@ __global__ __launch_bounds__(256, 2) void pod_decode_kernel(KernelArgs a) {
   POD_DECODE_BUFFERS(wave)
   if (d < a.n_d) {
     const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
-    decode_unit<KVM>(a, (cptr)a.d_items + d * D_FIELDS, db0, db1);
+    int ticket;
+    decode_unit<KVM>(a, (cptr)a.d_items + d * D_FIELDS, db0, db1, nullptr, ticket);
     if (a.trace && (threadIdx.x & 63) == 0) trace_unit(a, a.n_p + d, 1, d, cu_slot_id(), t0);
   }
 }
