@@ -237,7 +237,8 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
   const int32_t qchunks = (int32_t)ceil_div(g, kDecodeRows);
   double total_keys = 0.0;
   for (int32_t k : b.dkv) total_keys += double(k) * hkv * qchunks;
-  int64_t chunk = kMinDecodeChunk;
+  int64_t chunk =
+      total_keys >= double(decode_wave_slots) * kMinDecodeChunk ? kMinDecodeChunk : kMinDecodeChunkSmall;
   if (decode_wave_slots > 0 && total_keys > 0) {
     const int64_t c =
         (int64_t)std::ceil(total_keys / double(std::max(1, d_units_per_slot) * decode_wave_slots));

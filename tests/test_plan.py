@@ -260,3 +260,17 @@ def test_forced_splits_are_capped_at_64():
     assert len(D) == 2 * 64                     # 2 kv heads x 64 splits
     M = pl.export(2).reshape(-1, M_F)
     assert int((M[:, 3] & 0xFFFF).max()) == 64
+
+
+def test_decode_chunk_floor_follows_batch_size():
+    # enough decode keys for every decode wavefront: chunks of >= 512 keys
+    # (only a request's remainder is shorter); too few: chunks down to 128
+    tiny = inputs.config_spec("tiny")
+    D = _spec_lists(tiny).export(1).reshape(-1, D_F)
+    assert (D[:, 4] - D[:, 3]).max() <= 128
+    spec = inputs.config_spec("llama3_8b")
+    D = _spec_lists(spec).export(1).reshape(-1, D_F)
+    for i, kv in enumerate(spec.decode_kv_len):
+        d = D[D[:, 0] == i]
+        n_split = len(d) // spec.num_kv_heads
+        assert n_split <= -(-kv // 512), (i, kv, n_split)
