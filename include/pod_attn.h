@@ -103,10 +103,14 @@ typedef struct {
 typedef struct {
   int32_t wgs_per_cu;            /* 0 = auto; only 2 is supported (one
                                     prefill-capable wave per SIMD pair) */
-  int32_t prefill_quarters_per_cu; /* target prefill workgroups per CU in
-                                    quarters (0..4*wgs_per_cu); -1 = auto
-                                    (proportional to the estimated prefill
-                                    and decode times, [POD] "The idea") */
+  int32_t prefill_quarters_per_cu; /* prefill share q in 0..4*wgs_per_cu
+                                    (eighths of the workgroup slots); -1 =
+                                    auto (proportional to the estimated
+                                    prefill and decode times, [POD] "The
+                                    idea").  SPLIT: the CUs whose index in
+                                    their shader array is below q start on
+                                    prefill; COLOCATE: the first q/4 of each
+                                    CU's workgroups do */
   int32_t prefill_kv_splits;     /* 0 = auto; >0 forces this many KV splits per
                                     prefill tile (capped by its 64-key tiles and
                                     by 64) */
