@@ -35,9 +35,12 @@ Pins (tests/test_oracle*.py, all ``-m "not gpu"``): brute force with
 returning its value exactly, a decode row equal to the last prefill row,
 split/merge invariance, the identical-keys closed form, a boundary probe,
 GQA == MHA with repeated KV heads, ``torch`` float64 SDPA with an explicit
-mask, page-table invariance, and hand-derived worked examples under
-``tests/golden/``.  Planted-mistake tests check that each plausible bug in
-the oracle is caught by at least one pin.
+mask, page-table invariance, and the row-sampling entry point against brute
+force and against the whole-batch oracle.  Planted-mistake tests check that
+each plausible bug in the oracle is caught by at least one pin.  The pages
+print no worked example with numbers, so ``tests/golden/`` holds only a
+regression snapshot written from this oracle by ``make_golden.py``; it pins
+nothing.
 """
 
 from .attention import (  # noqa: F401

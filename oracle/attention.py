@@ -256,6 +256,13 @@ def _prefill_offsets(batch):
     return np.concatenate([[0], np.cumsum(qo)])
 
 
+def _request_of_row(offs: np.ndarray, g: int) -> int:
+    """Prefill request holding global query row ``g``: the r with
+    offs[r] <= g < offs[r + 1] (``offs`` = [0, qo_0, qo_0 + qo_1, ...]).  A
+    chunk's first row belongs to that chunk, not to the one before it."""
+    return int(np.searchsorted(offs, g, side="right") - 1)
+
+
 def batch_attention(batch: Dict, workers: Optional[int] = None,
                     row_block: int = 256) -> Dict[str, np.ndarray]:
     """Oracle outputs for every row of a hybrid batch.
@@ -338,13 +345,15 @@ def sample_batch_attention(batch: Dict, prefill_rows: Sequence[int],
     n_p = len(qo)
     prefill_rows = [int(x) for x in prefill_rows]
     decode_ids = [int(x) for x in decode_ids]
+    if any(g < 0 or g >= offs[-1] for g in prefill_rows) or \
+            any(i < 0 or i >= len(dkv) for i in decode_ids):
+        raise ValueError("sampled row or decode id out of range")
     res_p = {}
     res_d = {}
 
     by_req: Dict[int, List[int]] = {}
     for g in prefill_rows:
-        r = int(np.searchsorted(offs, g, side="right") - 1)
-        by_req.setdefault(r, []).append(g)
+        by_req.setdefault(_request_of_row(offs, g), []).append(g)
 
     jobs = []
     for r, rows in by_req.items():

@@ -19,6 +19,11 @@ What each pin rests on:
   sdpa            torch float64 scaled_dot_product_attention, explicit mask
   page_invariance the paged gather == the same tokens stored contiguously
   bf16_upcast     known bfloat16 bit patterns
+  sample_rows_bruteforce  the row-sampling entry point against the loop
+                  definition on tiny batches (every chunk's first and last
+                  row, decodes in shuffled order)
+  sample_rows_match_batch the row-sampling entry point against the whole-batch
+                  oracle on a paged batch of several chunks and decodes
 """
 
 import math
@@ -305,7 +310,64 @@ def pin_bf16_upcast():
         assert g_ == w, (g_, w)
 
 
+def _chunk_edge_rows(qo_lens, rng, extra=2):
+    """Every chunk's first, second, last and second-to-last rows plus a few
+    random rows (global row indices), shuffled."""
+    offs = np.concatenate([[0], np.cumsum(qo_lens)]).astype(int)
+    rows = set()
+    for r in range(len(qo_lens)):
+        a, b = int(offs[r]), int(offs[r + 1])
+        rows.update([a, min(a + 1, b - 1), b - 1, max(a, b - 2)])
+        rows.update(int(x) for x in rng.integers(a, b, size=min(extra, b - a)))
+    rows = sorted(rows)
+    rng.shuffle(rows)
+    return rows
+
+
+def pin_sample_rows_bruteforce():
+    rng = np.random.default_rng(31)
+    for spec in _tiny_specs():
+        b = inputs.make_batch_host(spec)
+        n_p = spec.num_prefill
+        offs = np.concatenate([[0], np.cumsum(spec.prefill_qo_len)]).astype(int)
+        rows = _chunk_edge_rows(spec.prefill_qo_len, rng)
+        dec = list(rng.permutation(spec.num_decode))
+        out = oracle.sample_batch_attention(b, rows, dec, workers=1)
+        assert list(out["prefill_rows"]) == rows and list(out["decode_ids"]) == dec
+        brute = {}
+        for r in range(n_p + spec.num_decode):
+            q, k, v, qo, L = _request_lists(b, r)
+            brute[r] = brute_attention(q, k, v, L, qo, spec.num_qo_heads,
+                                       spec.num_kv_heads, spec.causal, spec.sm_scale)
+        for t, g in enumerate(rows):
+            r = int(np.nonzero(offs[1:] > g)[0][0])           # offs[r] <= g < offs[r+1]
+            bo, bl = brute[r]
+            assert np.max(np.abs(out["o_prefill"][t] - np.array(bo[g - offs[r]]))) <= 1e-12, \
+                (spec.name, g)
+            assert np.max(np.abs(out["lse_prefill"][t] - np.array(bl[g - offs[r]]))) <= 1e-12
+        for t, i in enumerate(dec):
+            bo, bl = brute[n_p + int(i)]
+            assert np.max(np.abs(out["o_decode"][t] - np.array(bo[0]))) <= 1e-12, (spec.name, i)
+            assert np.max(np.abs(out["lse_decode"][t] - np.array(bl[0]))) <= 1e-12
+
+
+def pin_sample_rows_match_batch():
+    rng = np.random.default_rng(32)
+    spec = inputs.custom_spec("samp", 8, 2, [(37, 200), (1, 64), (90, 90), (64, 300)],
+                              [1, 17, 300, 64, 129], seed=33, head_dim=16, page_size=8,
+                              extra_pages=3)
+    b = inputs.make_batch_host(spec)
+    full = oracle.batch_attention(b, workers=1)
+    rows = _chunk_edge_rows(spec.prefill_qo_len, rng, extra=4)
+    dec = [4, 0, 2, 3, 1]
+    out = oracle.sample_batch_attention(b, rows, dec, workers=2)
+    for key, idx in (("o_prefill", rows), ("lse_prefill", rows), ("o_decode", dec),
+                     ("lse_decode", dec)):
+        assert np.all(np.isfinite(out[key])), key
+        assert np.max(np.abs(out[key] - full[key][idx])) <= 1e-13, key
+
+
 ALL_PINS = [pin_bruteforce, pin_rows_sum_to_one, pin_single_key,
             pin_decode_is_last_prefill_row, pin_split_merge, pin_identical_keys,
             pin_boundary_probe, pin_gqa_is_mha, pin_sdpa, pin_page_invariance,
-            pin_bf16_upcast]
+            pin_bf16_upcast, pin_sample_rows_bruteforce, pin_sample_rows_match_batch]

@@ -52,6 +52,9 @@ MUTANTS = {
                          .view(np.float32).astype(np.float64)),
     "kv_swapped": ("gather_request_kv", _swap_kv),
     "merge_unnormalised": ("merge_partials", _merge_no_norm),
+    # a chunk's first row handed to the request before it
+    "sample_row_to_previous_request": (
+        "_request_of_row", lambda offs, g: int(np.searchsorted(offs, g, side="left") - 1)),
 }
 
 
