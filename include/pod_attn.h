@@ -87,6 +87,8 @@ typedef enum {
 /* tuning flags */
 #define POD_FLAG_TRACE 0x1u   /* fused run (and, with match_sequential, sequential
                                  run) records one pod_trace_record_t per unit */
+#define POD_FLAG_BATCHED_PREFILL 0x2u  /* the plan also builds (and its workspace
+                                 holds) the work list of pod_attn_batched_prefill_run */
 
 typedef struct pod_attn_plan_s* pod_attn_plan_t;   /* opaque, library-owned */
 
@@ -101,8 +103,13 @@ typedef struct {
 } pod_attn_params_t;
 
 typedef struct {
-  int32_t wgs_per_cu;            /* 0 = auto; only 2 is supported (one
-                                    prefill-capable wave per SIMD pair) */
+  int32_t wgs_per_cu;            /* 0 = auto; only 2 is supported.  The pages
+                                    run 2 or 4 blocks per SM ([POD] "How
+                                    POD-Attention overlaps" > "Balance shared
+                                    memory and threadblock count"); here a
+                                    prefill workgroup needs 64 KiB of LDS and
+                                    256 VGPRs per lane, so only two fit a CU
+                                    (4 returns POD_ERR_UNSUPPORTED) */
   int32_t prefill_quarters_per_cu; /* prefill share q in 0..4*wgs_per_cu
                                     (eighths of the workgroup slots); -1 =
                                     auto (proportional to the estimated
@@ -167,7 +174,10 @@ typedef struct {
  *   lse_prefill, lse_decode device fp32 [rows, Hq], natural log; may be NULL
  * Request order everywhere: the prefill requests, then the decodes.  Slots of
  * pages past a request's kv_len are never read.  Base pointers must be 16-byte
- * aligned. */
+ * aligned.  Unlike common paged-attention interfaces there is no per-request
+ * last_page_len array: each request's kv_len is fixed when the plan is made
+ * (the work lists are built from it), and the run reads no length from these
+ * tensors. */
 typedef struct {
   const void* q_prefill;
   const void* q_decode;
@@ -182,7 +192,13 @@ typedef struct {
   float* lse_decode;
 } pod_attn_tensors_t;
 
-/* Plans one hybrid batch for the current HIP device.
+/* Plans one hybrid batch for the current HIP device: validates the lengths,
+ * builds the prefill tiles and decode units with their KV splits, and picks
+ * the prefill:decode share of the GPU in proportion to the estimated prefill
+ * and decode times ([POD] "The idea": proportional rather than even
+ * allocation; "How POD-Attention overlaps" > "Cap prefill splitting to avoid
+ * contention"; [PR] description: with at most 1536 prefill tokens the split
+ * count is sized for the slots left beside the co-located decode work).
  *   prefill_qo_len/prefill_kv_len: host int32 [num_prefill], 1 <= qo <= kv
  *   decode_kv_len: host int32 [num_decode], >= 1
  *   tuning: host, may be NULL (all automatic)
@@ -240,6 +256,46 @@ pod_status_t pod_attn_run_events(pod_attn_plan_t plan, const pod_attn_tensors_t*
 pod_status_t pod_attn_sequential_run(pod_attn_plan_t plan, const pod_attn_tensors_t* t,
                                      hipStream_t stream);
 
+/* Comparator of the pages: the sequential baseline's prefill kernel and
+ * decode kernel launched on two streams so that the hardware may run them
+ * concurrently ([POD] "What people did before, and where it broke": separate
+ * kernels on concurrent streams give no control over co-location), then the
+ * merge.  `decode_stream` (a different stream of default priority) first
+ * waits for the work already enqueued on `stream`; the prefill kernel and the
+ * merge run on `stream`, which waits for the decode kernel before the merge,
+ * so work enqueued on `stream` afterwards sees the whole result.  Uses the
+ * sequential plan's work lists.  Errors as pod_attn_run, plus
+ * POD_ERR_INVALID_ARGUMENT when both streams are the same. */
+pod_status_t pod_attn_streams_run(pod_attn_plan_t plan, const pod_attn_tensors_t* t,
+                                  hipStream_t stream, hipStream_t decode_stream);
+
+/* Comparator of the pages ("Batched Prefill" in the [PR] benchmark log): every
+ * request of the batch goes through the prefill kernel in one launch, each
+ * decode as a one-row chunk (a tile of its packed query heads at position
+ * kv_len - 1), followed by the merge.  The plan must have been made with
+ * POD_FLAG_BATCHED_PREFILL.  Errors as pod_attn_run, plus
+ * POD_ERR_INVALID_ARGUMENT for a plan without that flag. */
+pod_status_t pod_attn_batched_prefill_run(pod_attn_plan_t plan, const pod_attn_tensors_t* t,
+                                          hipStream_t stream);
+
+/* Log-sum-exp merge of KV-split partials ([PAT] abstract: the final merge of
+ * per-split results by online softmax; [POD] "Cap prefill splitting to avoid
+ * contention": attention split along the KV dimension).  For each row r:
+ *     M = max_s lse_s,  L = M + ln sum_s exp(lse_s - M),
+ *     O = sum_s exp(lse_s - L) * o_s
+ * where partials with lse_s = -inf weigh nothing; a row whose partials are
+ * all -inf gives O = 0 and L = -inf.
+ *   part_o   device fp32 [n_rows, n_splits, 128], each partial normalised
+ *            by its own softmax sum (16-byte aligned)
+ *   part_lse device fp32 [n_rows, n_splits], natural log
+ *   o        device bf16 [n_rows, 128] (16-byte aligned), written
+ *   lse      device fp32 [n_rows], natural log, written; may be NULL
+ * n_splits in [1, 64]; n_rows = 0 enqueues nothing.  Asynchronous on
+ * `stream`.  Errors: POD_ERR_INVALID_ARGUMENT (counts, NULL or misaligned
+ * pointers), POD_ERR_UNSUPPORTED (n_rows * n_splits >= 2^31), POD_ERR_HIP. */
+pod_status_t pod_attn_merge(const float* part_o, const float* part_lse, int32_t n_rows,
+                            int32_t n_splits, void* o, float* lse, hipStream_t stream);
+
 /* Counts of a plan.  Errors: POD_ERR_INVALID_ARGUMENT on NULL. */
 pod_status_t pod_attn_plan_info(pod_attn_plan_t plan, pod_attn_plan_info_t* out);
 
@@ -247,7 +303,8 @@ pod_status_t pod_attn_plan_info(pod_attn_plan_t plan, pod_attn_plan_info_t* out)
  * elements); *count receives the element count (dst may be NULL to query).
  * which: 0 fused prefill items (8 int32 each), 1 fused decode items (8 each),
  * 2 fused merge tasks (4 each), 3/4/5 the sequential lists, 6/7 the fused /
- * sequential prefill pool offsets (num_xcds + 1 each).  Item fields are
+ * sequential prefill pool offsets (num_xcds + 1 each), 8/9/10 the
+ * batched-prefill items, merge tasks and pool offsets.  Item fields are
  * documented in plan.h of the sources.  Errors: POD_ERR_INVALID_ARGUMENT. */
 pod_status_t pod_attn_plan_export(pod_attn_plan_t plan, int32_t which,
                                   int32_t* dst, size_t n, size_t* count);

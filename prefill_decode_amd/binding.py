@@ -23,10 +23,12 @@ STATUS = {0: "POD_OK", 1: "POD_ERR_INVALID_ARGUMENT", 2: "POD_ERR_UNSUPPORTED",
 KV_CONTIGUOUS, KV_PAGED = 0, 1
 SCHED_AUTO, SCHED_COLOCATE, SCHED_ORDERED, SCHED_SPLIT = 0, 1, 2, 3
 FLAG_TRACE = 0x1
+FLAG_BATCHED_PREFILL = 0x2
 
 # every function the header declares
 EXPORTED = ("pod_attn_plan", "pod_attn_plan_host", "pod_attn_run", "pod_attn_run_events",
-            "pod_attn_sequential_run",
+            "pod_attn_sequential_run", "pod_attn_streams_run", "pod_attn_batched_prefill_run",
+            "pod_attn_merge",
             "pod_attn_plan_info", "pod_attn_plan_export", "pod_attn_read_trace",
             "pod_attn_plan_destroy", "pod_attn_last_error", "pod_attn_probe_hwid")
 
@@ -100,6 +102,11 @@ def lib():
         L.pod_attn_run_events.argtypes = [C.c_void_p, C.POINTER(Tensors), C.c_void_p,
                                           C.c_void_p, C.c_void_p]
         L.pod_attn_sequential_run.argtypes = [C.c_void_p, C.POINTER(Tensors), C.c_void_p]
+        L.pod_attn_streams_run.argtypes = [C.c_void_p, C.POINTER(Tensors), C.c_void_p,
+                                           C.c_void_p]
+        L.pod_attn_batched_prefill_run.argtypes = [C.c_void_p, C.POINTER(Tensors), C.c_void_p]
+        L.pod_attn_merge.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p,
+                                     C.c_void_p, C.c_void_p]
         L.pod_attn_plan_info.argtypes = [C.c_void_p, C.POINTER(PlanInfo)]
         L.pod_attn_plan_export.argtypes = [C.c_void_p, C.c_int32, i32p, C.c_size_t,
                                            C.POINTER(C.c_size_t)]
@@ -268,6 +275,29 @@ def sequential_run(p: Plan, tensors: Tensors, stream=None):
     _check(lib().pod_attn_sequential_run(p.handle, C.byref(tensors), _stream(stream)))
 
 
+def streams_run(p: Plan, tensors: Tensors, decode_stream, stream=None):
+    """Prefill kernel on `stream`, decode kernel on `decode_stream`, merge on
+    `stream` after both (asynchronous)."""
+    _check(lib().pod_attn_streams_run(p.handle, C.byref(tensors), _stream(stream),
+                                      _stream(decode_stream)))
+
+
+def batched_prefill_run(p: Plan, tensors: Tensors, stream=None):
+    """Every request through the prefill kernel (decodes as one-row chunks),
+    then the merge; the plan needs FLAG_BATCHED_PREFILL (asynchronous)."""
+    _check(lib().pod_attn_batched_prefill_run(p.handle, C.byref(tensors), _stream(stream)))
+
+
+def merge(part_o, part_lse, o, lse=None, stream=None):
+    """Log-sum-exp merge of fp32 partials [rows, splits, 128] / LSEs [rows,
+    splits] (natural log) into bf16 o [rows, 128] and fp32 lse [rows]."""
+    rows, splits = int(part_lse.shape[0]), int(part_lse.shape[1])
+    assert tuple(part_o.shape) == (rows, splits, 128) and part_o.is_contiguous()
+    assert part_lse.is_contiguous() and tuple(o.shape) == (rows, 128) and o.is_contiguous()
+    _check(lib().pod_attn_merge(_dp(part_o), _dp(part_lse), rows, splits, _dp(o), _dp(lse),
+                                _stream(stream)))
+
+
 def probe_hwid(num_blocks: int, device="cuda", stream=None) -> np.ndarray:
     import torch
     out = torch.zeros(2 * num_blocks, dtype=torch.int32, device=device)
@@ -329,6 +359,12 @@ class BatchRunner:
 
     def sequential_run(self, stream=None):
         sequential_run(self.plan, self.tensors, stream)
+
+    def streams_run(self, decode_stream, stream=None):
+        streams_run(self.plan, self.tensors, decode_stream, stream)
+
+    def batched_prefill_run(self, stream=None):
+        batched_prefill_run(self.plan, self.tensors, stream)
 
     def outputs(self):
         """Host copies: O as float64 (from bf16) and LSE as float64."""

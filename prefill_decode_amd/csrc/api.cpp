@@ -41,16 +41,24 @@ struct pod_attn_plan_s {
   pod_device_desc_t dev{};
   PlanChoice choice;
   WorkLists fused, seq;
+  WorkLists bp;                // batched-prefill comparator (POD_FLAG_BATCHED_PREFILL)
   bool seq_is_fused = false;
+  bool has_bp = false;
   int32_t n_partials = 0;
   int32_t trace_records = 0;
   // workspace layout (bytes)
   size_t off_counters = 0, off_trace = 0, off_part_lse = 0, off_part_o = 0;
-  DevLists dl_fused, dl_seq;
+  DevLists dl_fused, dl_seq, dl_bp;
+  // two-stream comparator: fork / join events (created on first use)
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   uint64_t launches[2] = {0, 0};   // successful launches per kind (counter parity)
   size_t ws_bytes = 0;
   char* ws = nullptr;          // caller-owned device buffer (NULL: host-only plan)
   int device = -1;
+  ~pod_attn_plan_s() {
+    if (ev_fork) (void)hipEventDestroy(ev_fork);
+    if (ev_join) (void)hipEventDestroy(ev_join);
+  }
 };
 
 namespace {
@@ -100,7 +108,13 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
     build_lists(pl->batch, dev, slots, kSeqPrefillHalfItemsPerSlot, slots * kWavesPerWG, kSeqDecodeUnitsPerWave,
                 t.prefill_kv_splits, t.decode_kv_splits, &pl->seq);
   const WorkLists& sq = pl->seq_is_fused ? pl->fused : pl->seq;
-  pl->n_partials = std::max(pl->fused.n_partials, sq.n_partials);
+  // Batched-prefill comparator: every request through the prefill kernel,
+  // split like the sequential plan's prefill.
+  pl->has_bp = (t.flags & POD_FLAG_BATCHED_PREFILL) != 0;
+  if (pl->has_bp)
+    build_lists(pl->batch, dev, slots, kSeqPrefillHalfItemsPerSlot, 0, 1, t.prefill_kv_splits, 0,
+                &pl->bp, /*decodes_as_prefill=*/true);
+  pl->n_partials = std::max(std::max(pl->fused.n_partials, sq.n_partials), pl->bp.n_partials);
   pl->trace_records = (t.flags & POD_FLAG_TRACE) ? pl->fused.n_p() + pl->fused.n_d() : 0;
 
   // workspace layout
@@ -118,12 +132,13 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   place(pl->fused, pl->dl_fused);
   if (pl->seq_is_fused) pl->dl_seq = pl->dl_fused;
   else place(pl->seq, pl->dl_seq);
+  if (pl->has_bp) place(pl->bp, pl->dl_bp);
   pl->off_trace = off;
   off = align_up(off + (size_t)pl->trace_records * sizeof(pod_trace_record_t));
   pl->off_part_lse = off;
   off = align_up(off + (size_t)pl->n_partials * sizeof(float));
   pl->off_part_o = off;
-  off = align_up(off + (size_t)pl->n_partials * kHeadDim * sizeof(uint16_t));
+  off = align_up(off + (size_t)pl->n_partials * kHeadDim * sizeof(float));
   pl->ws_bytes = off;
   return POD_OK;
 }
@@ -226,7 +241,7 @@ KernelArgs make_args(const pod_attn_plan_s* pl, const pod_attn_tensors_t* t, con
   a.o_decode = (uint16_t*)t->o_decode;
   a.lse_prefill = t->lse_prefill;
   a.lse_decode = t->lse_decode;
-  a.part_o = (uint16_t*)(pl->ws + pl->off_part_o);
+  a.part_o = (float*)(pl->ws + pl->off_part_o);
   a.part_lse = (float*)(pl->ws + pl->off_part_lse);
   a.p_items = (const int32_t*)(pl->ws + dl.p_items);
   a.d_items = (const int32_t*)(pl->ws + dl.d_items);
@@ -252,7 +267,16 @@ KernelArgs make_args(const pod_attn_plan_s* pl, const pod_attn_tensors_t* t, con
   a.wgs_per_cu = pl->choice.wgs_per_cu;
   a.prefill_quarters = pl->choice.prefill_quarters;
   a.sched_mode = pl->choice.sched_mode;
+  a.n_preq = (int32_t)pl->batch.qo.size();
+  a.merge_splits = 0;
+  a.merge_lse_scale = 1.0f;
   return a;
+}
+
+pod_status_t launch_merge_of(const KernelArgs& a, const WorkLists& w, hipStream_t stream) {
+  if (w.n_m() == 0) return POD_OK;
+  hipError_t e = launch_merge(a, (w.n_m() + kMergeTasksPerWG - 1) / kMergeTasksPerWG, stream);
+  return e == hipSuccess ? POD_OK : hip_err(e, "merge kernel launch");
 }
 
 }  // namespace
@@ -344,7 +368,9 @@ pod_status_t pod_attn_plan(const pod_attn_params_t* params, int32_t num_prefill,
     if ((s2 = upload(pl->ws, d.d_items, w.d_items, stream)) != POD_OK) return s2;
     return upload(pl->ws, d.m_tasks, w.m_tasks, stream);
   };
-  if ((st = up(pl->fused, pl->dl_fused)) != POD_OK || (!pl->seq_is_fused && (st = up(pl->seq, pl->dl_seq)) != POD_OK)) {
+  if ((st = up(pl->fused, pl->dl_fused)) != POD_OK ||
+      (!pl->seq_is_fused && (st = up(pl->seq, pl->dl_seq)) != POD_OK) ||
+      (pl->has_bp && (st = up(pl->bp, pl->dl_bp)) != POD_OK)) {
     delete pl;
     return st;
   }
@@ -374,11 +400,7 @@ pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t
   }
   if (after_fused && (e = hipEventRecord(after_fused, stream)) != hipSuccess)
     return hip_err(e, "hipEventRecord(after_fused)");
-  if (w.n_m() > 0) {
-    e = launch_merge(a, (w.n_m() + kMergeTasksPerWG - 1) / kMergeTasksPerWG, stream);
-    if (e != hipSuccess) return hip_err(e, "merge kernel launch");
-  }
-  return POD_OK;
+  return launch_merge_of(a, w, stream);
 }
 
 pod_status_t pod_attn_run(pod_attn_plan_t pl, const pod_attn_tensors_t* t, hipStream_t stream) {
@@ -406,11 +428,82 @@ pod_status_t pod_attn_sequential_run(pod_attn_plan_t pl, const pod_attn_tensors_
     hipError_t e = launch_decode(a, kvm, w.n_groups(), stream);
     if (e != hipSuccess) return hip_err(e, "decode kernel launch");
   }
-  if (w.n_m() > 0) {
-    hipError_t e = launch_merge(a, (w.n_m() + kMergeTasksPerWG - 1) / kMergeTasksPerWG, stream);
-    if (e != hipSuccess) return hip_err(e, "merge kernel launch");
+  return launch_merge_of(a, w, stream);
+}
+
+pod_status_t pod_attn_streams_run(pod_attn_plan_t pl, const pod_attn_tensors_t* t,
+                                  hipStream_t stream, hipStream_t decode_stream) {
+  pod_status_t st = check_tensors(pl, t);
+  if (st != POD_OK) return st;
+  if (decode_stream == stream)
+    return set_err(POD_ERR_INVALID_ARGUMENT, "decode_stream must differ from stream");
+  const WorkLists& w = pl->seq_is_fused ? pl->fused : pl->seq;
+  KernelArgs a = make_args(pl, t, w, pl->dl_seq);
+  pick_counters(pl, kKindSeq, stream, &a);
+  hipError_t e;
+  for (hipEvent_t* ev : {&pl->ev_fork, &pl->ev_join})
+    if (!*ev && (e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess)
+      return hip_err(e, "hipEventCreateWithFlags");
+  // the decode stream starts after the work already enqueued on `stream`
+  if ((e = hipEventRecord(pl->ev_fork, stream)) != hipSuccess) return hip_err(e, "hipEventRecord");
+  if ((e = hipStreamWaitEvent(decode_stream, pl->ev_fork, 0)) != hipSuccess)
+    return hip_err(e, "hipStreamWaitEvent");
+  const int kvm = kv_mode_of(pl);
+  if (w.n_p() > 0) {
+    if ((e = launch_prefill(a, kvm, w.n_p(), stream)) != hipSuccess)
+      return hip_err(e, "prefill kernel launch");
+    if (!a.self_reset) ++pl->launches[kKindSeq];
   }
-  return POD_OK;
+  if (w.n_groups() > 0 && (e = launch_decode(a, kvm, w.n_groups(), decode_stream)) != hipSuccess)
+    return hip_err(e, "decode kernel launch");
+  // join: the merge (and whatever the caller enqueues next) waits for both
+  if ((e = hipEventRecord(pl->ev_join, decode_stream)) != hipSuccess)
+    return hip_err(e, "hipEventRecord");
+  if ((e = hipStreamWaitEvent(stream, pl->ev_join, 0)) != hipSuccess)
+    return hip_err(e, "hipStreamWaitEvent");
+  return launch_merge_of(a, w, stream);
+}
+
+pod_status_t pod_attn_batched_prefill_run(pod_attn_plan_t pl, const pod_attn_tensors_t* t,
+                                          hipStream_t stream) {
+  pod_status_t st = check_tensors(pl, t);
+  if (st != POD_OK) return st;
+  if (!pl->has_bp)
+    return set_err(POD_ERR_INVALID_ARGUMENT, "plan was made without POD_FLAG_BATCHED_PREFILL");
+  const WorkLists& w = pl->bp;
+  KernelArgs a = make_args(pl, t, w, pl->dl_bp);
+  pick_counters(pl, kKindSeq, stream, &a);
+  if (w.n_p() > 0) {
+    hipError_t e = launch_prefill(a, kv_mode_of(pl), w.n_p(), stream, /*batched=*/true);
+    if (e != hipSuccess) return hip_err(e, "batched prefill kernel launch");
+    if (!a.self_reset) ++pl->launches[kKindSeq];
+  }
+  return launch_merge_of(a, w, stream);
+}
+
+pod_status_t pod_attn_merge(const float* part_o, const float* part_lse, int32_t n_rows,
+                            int32_t n_splits, void* o, float* lse, hipStream_t stream) {
+  if (n_rows < 0 || n_splits < 1 || n_splits > kMaxMergeSplits)
+    return set_err(POD_ERR_INVALID_ARGUMENT, "n_rows must be >= 0 and n_splits in [1, 64]");
+  if ((int64_t)n_rows * n_splits > (int64_t)INT32_MAX)
+    return set_err(POD_ERR_UNSUPPORTED, "too many partials");
+  if (n_rows == 0) return POD_OK;
+  if (!part_o || !part_lse || !o)
+    return set_err(POD_ERR_INVALID_ARGUMENT, "part_o, part_lse or o is NULL");
+  if (!aligned16(part_o) || !aligned16(o))
+    return set_err(POD_ERR_INVALID_ARGUMENT, "part_o and o must be 16-byte aligned");
+  KernelArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.part_o = const_cast<float*>(part_o);
+  a.part_lse = const_cast<float*>(part_lse);
+  a.o_prefill = (uint16_t*)o;
+  a.lse_prefill = lse;
+  a.m_tasks = nullptr;
+  a.n_m = n_rows;
+  a.merge_splits = n_splits;
+  a.merge_lse_scale = 1.4426950408889634f;
+  hipError_t e = launch_merge(a, (n_rows + kMergeTasksPerWG - 1) / kMergeTasksPerWG, stream);
+  return e == hipSuccess ? POD_OK : hip_err(e, "merge kernel launch");
 }
 
 pod_status_t pod_attn_plan_info(pod_attn_plan_t pl, pod_attn_plan_info_t* out) {
@@ -448,6 +541,9 @@ pod_status_t pod_attn_plan_export(pod_attn_plan_t pl, int32_t which, int32_t* ds
     case 5: v = &sq.m_tasks; break;
     case 6: v = &pl->fused.pool_off; break;
     case 7: v = &sq.pool_off; break;
+    case 8: v = &pl->bp.p_items; break;
+    case 9: v = &pl->bp.m_tasks; break;
+    case 10: v = &pl->bp.pool_off; break;
     default: return set_err(POD_ERR_INVALID_ARGUMENT, "unknown list id");
   }
   *count = v->size();

@@ -52,8 +52,9 @@ struct KernelArgs {
   uint16_t* o_decode;
   float* lse_prefill;
   float* lse_decode;
-  uint16_t* part_o;       // [n_partials, 128] bf16 (each partial divided by its own l)
-  float* part_lse;        // [n_partials] fp32, log2 domain
+  float* part_o;          // [n_partials, 128] fp32 (each partial divided by its own l)
+  float* part_lse;        // [n_partials] fp32, log2 domain (natural log for a
+                          // standalone merge, see merge_lse_scale)
   const int32_t* p_items;
   const int32_t* d_items;
   const int32_t* m_tasks;
@@ -71,10 +72,17 @@ struct KernelArgs {
   int32_t causal;
   float scale_log2;       // sm_scale * log2(e)
   int32_t wgs_per_cu, prefill_quarters, sched_mode;
+  int32_t n_preq;         // prefill requests: items with a larger KV request index are
+                          // decode requests run through the prefill tile (batched prefill)
+  // standalone merge (m_tasks == NULL): task t combines partials t * merge_splits
+  // .. + merge_splits - 1 into row t of o_prefill / lse_prefill
+  int32_t merge_splits;
+  float merge_lse_scale;  // factor taking part_lse to log2 (1, or log2(e) for natural log)
 };
 
 hipError_t launch_fused(const KernelArgs& a, int kv_mode, int grid, hipStream_t s);
-hipError_t launch_prefill(const KernelArgs& a, int kv_mode, int grid, hipStream_t s);
+hipError_t launch_prefill(const KernelArgs& a, int kv_mode, int grid, hipStream_t s,
+                          bool batched = false);
 hipError_t launch_decode(const KernelArgs& a, int kv_mode, int grid, hipStream_t s);
 hipError_t launch_merge(const KernelArgs& a, int grid, hipStream_t s);
 hipError_t launch_probe(int32_t* out, int blocks, hipStream_t s);

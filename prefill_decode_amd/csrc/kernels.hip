@@ -197,8 +197,13 @@ struct KvAddr {
 // operand, two MFMAs), the online softmax of both blocks, then O^T += V^T
 // P^T (one V^T operand, two MFMAs).  The loop over tiles is unrolled by two
 // so that every LDS address is a per-lane base plus an immediate offset.
+//
+// BP (batched prefill, a comparator of the pages): items whose KV request is
+// a decode request (index >= n_preq) read their query row from q_decode and
+// write o_decode / lse_decode, i.e. a decode runs through this tile as a
+// one-row chunk.
 // ---------------------------------------------------------------------------
-template <int KVM>
+template <int KVM, bool BP = false>
 __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char* __restrict__ kt0,
                                              char* __restrict__ kt1, char* __restrict__ vt0,
                                              char* __restrict__ vt1) {
@@ -214,6 +219,8 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   const int qrow0 = it[P_QROW0], head0 = it[P_HEAD], nrows = it[P_NROWS];
   const int pos0 = it[P_POS0], kv_begin = it[P_KV_BEGIN], kv_end = it[P_KV_END];
   const int kvreq = it[P_KVREQ], part = it[P_PART];
+  const bool dec_item = BP && kvreq >= a.n_preq;
+  const uint16_t* const q_src = dec_item ? a.q_decode : a.q_prefill;
   const int wph = kWavesPerWG / a.p_heads;          // waves per head
   const int hidx = wave / wph;
   const int wpos = kWaveRows * (wave - hidx * wph);  // first position (item-relative)
@@ -246,9 +253,9 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   const bool okA = rA < nrows, okB = rB < nrows;
   u32x4 qa[8], qb[8];
   {
-    const uint16_t* qpa = a.q_prefill +
+    const uint16_t* qpa = q_src +
         ((int64_t)(qrow0 + (okA ? rA : 0)) * a.hq + head) * kHeadDim + 8 * hl;
-    const uint16_t* qpb = a.q_prefill +
+    const uint16_t* qpb = q_src +
         ((int64_t)(qrow0 + (okB ? rB : 0)) * a.hq + head) * kHeadDim + 8 * hl;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
@@ -538,7 +545,9 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const float lse2 = l_tot > 0.0f ? m + log2_(l_tot) : kNegInf;
     if (part < 0) {
-      uint16_t* op = a.o_prefill + ((int64_t)(qrow0 + r) * a.hq + head) * kHeadDim + 4 * hl;
+      uint16_t* const o_dst = dec_item ? a.o_decode : a.o_prefill;
+      float* const lse_dst = dec_item ? a.lse_decode : a.lse_prefill;
+      uint16_t* op = o_dst + ((int64_t)(qrow0 + r) * a.hq + head) * kHeadDim + 4 * hl;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -547,19 +556,20 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
                            pack_bf16x2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv)};
           *(u32x2*)(op + 32 * db + 8 * g4) = w;
         }
-      if (hl == 0 && a.lse_prefill)
-        a.lse_prefill[(int64_t)(qrow0 + r) * a.hq + head] = lse2 * kLn2;
+      if (hl == 0 && lse_dst) lse_dst[(int64_t)(qrow0 + r) * a.hq + head] = lse2 * kLn2;
     } else {
+      // fp32 partial (already divided by its own l): the merge reweights
+      // partials whose sizes may differ by orders of magnitude, so they keep
+      // full precision until the final rounding
       const int pi = part + hidx * (kPrefillRows / a.p_heads) + r;
-      uint16_t* pp = a.part_o + (int64_t)pi * kHeadDim + 4 * hl;
+      float* pp = a.part_o + (int64_t)pi * kHeadDim + 4 * hl;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const u32x2 w = {pack_bf16x2(o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv),
-                           pack_bf16x2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv)};
-          *(u32x2*)(pp + 32 * db + 8 * g4) = w;
-        }
+        for (int g4 = 0; g4 < 4; ++g4)
+          *(f32x4*)(pp + 32 * db + 8 * g4) =
+              f32x4{o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv, o[db][4 * g4 + 2] * inv,
+                    o[db][4 * g4 + 3] * inv};
       if (hl == 0) a.part_lse[pi] = lse2;
     }
   };
@@ -813,13 +823,11 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
     if (q4 == 0 && a.lse_decode) a.lse_decode[(int64_t)qi * a.hq + h0 + j] = lse2 * kLn2;
   } else {
     const int pi = part + j * pstride;
-    uint16_t* pp = a.part_o + (int64_t)pi * kHeadDim + 4 * q4;
+    float* pp = a.part_o + (int64_t)pi * kHeadDim + 4 * q4;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const u32x2 w = {pack_bf16x2(o[db][0] * inv, o[db][1] * inv),
-                       pack_bf16x2(o[db][2] * inv, o[db][3] * inv)};
-      *(u32x2*)(pp + 16 * db) = w;
-    }
+    for (int db = 0; db < 8; ++db)
+      *(f32x4*)(pp + 16 * db) = f32x4{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv,
+                                      o[db][3] * inv};
     if (q4 == 0) a.part_lse[pi] = lse2;
   }
 }
@@ -1101,7 +1109,7 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
   finish_launch(a, &s_info[4]);
 }
 
-template <int KVM>
+template <int KVM, bool BP = false>
 __global__ __launch_bounds__(256, 2) void pod_prefill_kernel(KernelArgs a) {
   POD_LDS_OBJECTS
   zero_next_counters(a);
@@ -1114,7 +1122,7 @@ __global__ __launch_bounds__(256, 2) void pod_prefill_kernel(KernelArgs a) {
   __syncthreads();
   if (unit >= 0) {
     const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
-    prefill_tile<KVM>(a, (cptr)a.p_items + rfl(unit) * P_FIELDS, POD_PREFILL_BUFFERS);
+    prefill_tile<KVM, BP>(a, (cptr)a.p_items + rfl(unit) * P_FIELDS, POD_PREFILL_BUFFERS);
     if (a.trace && threadIdx.x == 0) trace_unit(a, unit, 0, unit, cu_slot_id(), t0);
   }
   finish_launch(a, &s_info[1]);
@@ -1137,28 +1145,51 @@ __global__ __launch_bounds__(256, 2) void pod_decode_kernel(KernelArgs a) {
 
 // Merge: one 16-lane group per (row, head) task, four tasks per wavefront.
 // Every load of a task -- its split LSEs (lane j holds splits j, j + 16, ..)
-// and its bf16 partial rows (16 lanes x 16 bytes = one row) -- is issued
-// before any arithmetic, so a task costs about one memory round trip.
-// Splits are summed in index order.
+// and its fp32 partial rows (16 lanes x 32 bytes = one 512-byte row) -- is
+// issued before any arithmetic, so a task costs about one memory round trip.
+// Splits are summed in index order.  With m_tasks == NULL the kernel merges
+// a caller's dense [rows, merge_splits] partials (pod_attn_merge).
 __global__ __launch_bounds__(256) void pod_merge_kernel(KernelArgs a) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, j = lane & 15;
   const int task = blockIdx.x * kMergeTasksPerWG + (threadIdx.x >> 6) * 4 + g;
   const bool live = task < a.n_m;
-  const u32x4 tf = *(const u32x4*)(a.m_tasks + (int64_t)(live ? task : 0) * M_FIELDS);
-  const int out = (int)tf[M_OUT], base = (int)tf[M_BASE], stride = (int)tf[M_STRIDE];
-  const int n = live ? (int)(tf[M_NFLAG] & 0xFFFFu) : 0;      // n <= 64
-  const bool is_dec = (tf[M_NFLAG] >> 16) != 0;
+  int out, base, stride, n;
+  bool is_dec;
+  if (a.m_tasks != nullptr) {
+    const u32x4 tf = *(const u32x4*)(a.m_tasks + (int64_t)(live ? task : 0) * M_FIELDS);
+    out = (int)tf[M_OUT];
+    base = (int)tf[M_BASE];
+    stride = (int)tf[M_STRIDE];
+    n = live ? (int)(tf[M_NFLAG] & 0xFFFFu) : 0;      // n <= 64
+    is_dec = (tf[M_NFLAG] >> 16) != 0;
+  } else {
+    out = live ? task : 0;
+    base = out * a.merge_splits;
+    stride = 1;
+    n = live ? a.merge_splits : 0;
+    is_dec = false;
+  }
+  const float lsc = a.merge_lse_scale;
   float ls[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
-    ls[c] = 16 * c + j < n ? a.part_lse[base + (16 * c + j) * stride] : kNegInf;
+    ls[c] = 16 * c + j < n ? a.part_lse[base + (16 * c + j) * stride] * lsc : kNegInf;
   constexpr int kBatch = 8;
-  const uint16_t* po = a.part_o + (int64_t)base * kHeadDim + 8 * j;
-  u32x4 v[kBatch];
+  const float* po = a.part_o + (int64_t)base * kHeadDim + 8 * j;
+  f32x4 v0[kBatch], v1[kBatch];
+  auto load_row = [&](int sp, int i) {
+    if (sp < n) {
+      const float* r = po + (int64_t)sp * stride * kHeadDim;
+      v0[i] = *(const f32x4*)r;
+      v1[i] = *(const f32x4*)(r + 4);
+    } else {
+      v0[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      v1[i] = v0[i];
+    }
+  };
 #pragma unroll
-  for (int i = 0; i < kBatch; ++i)
-    v[i] = i < n ? *(const u32x4*)(po + (int64_t)i * stride * kHeadDim) : u32x4{0, 0, 0, 0};
+  for (int i = 0; i < kBatch; ++i) load_row(i, i);
   // max and weight sum over the group's 16 lanes
   float m = fmax_(fmax_(ls[0], ls[1]), fmax_(ls[2], ls[3]));
 #pragma unroll
@@ -1182,9 +1213,7 @@ __global__ __launch_bounds__(256) void pod_merge_kernel(KernelArgs a) {
   for (int s0 = 0; s0 < nmax; s0 += kBatch) {
     if (s0 > 0) {
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i)
-        v[i] = s0 + i < n ? *(const u32x4*)(po + (int64_t)(s0 + i) * stride * kHeadDim)
-                          : u32x4{0, 0, 0, 0};
+      for (int i = 0; i < kBatch; ++i) load_row(s0 + i, i);
     }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
@@ -1194,8 +1223,8 @@ __global__ __launch_bounds__(256) void pod_merge_kernel(KernelArgs a) {
       const float wgt = sp < n ? __shfl(wsrc, 16 * g + (sp & 15)) : 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += wgt * __uint_as_float(v[i][e] << 16);
-        acc[2 * e + 1] += wgt * __uint_as_float(v[i][e] & 0xFFFF0000u);
+        acc[e] += wgt * v0[i][e];
+        acc[4 + e] += wgt * v1[i][e];
       }
     }
   }
@@ -1236,8 +1265,26 @@ hipError_t launch_fused(const KernelArgs& a, int kv_mode, int grid, hipStream_t 
   POD_DISPATCH(pod_fused_kernel, 0)
 }
 
-hipError_t launch_prefill(const KernelArgs& a, int kv_mode, int grid, hipStream_t s) {
-  POD_DISPATCH(pod_prefill_kernel, 0)
+template <bool BP>
+struct PrefillK {
+  template <int KVM>
+  static void launch(int grid, hipStream_t s, const KernelArgs& a) {
+    hipLaunchKernelGGL((pod_prefill_kernel<KVM, BP>), dim3(grid), dim3(256), 0, s, a);
+  }
+};
+
+hipError_t launch_prefill(const KernelArgs& a, int kv_mode, int grid, hipStream_t s, bool batched) {
+  auto go = [&](auto k) {
+    using K = decltype(k);
+    switch (kv_mode) {
+      case KV_CONTIG: K::template launch<KV_CONTIG>(grid, s, a); break;
+      case KV_PAGED_WIDE: K::template launch<KV_PAGED_WIDE>(grid, s, a); break;
+      default: K::template launch<KV_PAGED_NARROW>(grid, s, a); break;
+    }
+  };
+  if (batched) go(PrefillK<true>{});
+  else go(PrefillK<false>{});
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const KernelArgs& a, int kv_mode, int grid, hipStream_t s) {

@@ -134,7 +134,8 @@ int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu, int32_t sched_
 
 void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_slots,
                  int32_t p_half_items_per_slot, int64_t decode_wave_slots, int32_t d_units_per_slot,
-                 int32_t force_p_splits, int32_t force_d_splits, WorkLists* out) {
+                 int32_t force_p_splits, int32_t force_d_splits, WorkLists* out,
+                 bool decodes_as_prefill) {
   const auto& p = b.params;
   const int32_t hq = p.num_qo_heads, hkv = p.num_kv_heads, g = hq / hkv;
   const int32_t np = (int32_t)b.qo.size(), nd = (int32_t)b.dkv.size();
@@ -163,6 +164,13 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
       }
     qrow += qo;
   }
+  if (decodes_as_prefill) {
+    for (int32_t i = 0; i < nd; ++i)
+      for (int32_t h = 0; h < hq; h += nh) {
+        const int32_t kv = b.dkv[i];
+        tiles.push_back(Tile{i, h, 1, kv - 1, kv, np + i, h / g});
+      }
+  }
   // order: KV head major, so that one XCD pool holds the tiles sharing K/V
   std::stable_sort(tiles.begin(), tiles.end(), [](const Tile& a, const Tile& c) {
     return a.kvh < c.kvh;
@@ -185,6 +193,7 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
     const int32_t per = (int32_t)ceil_div(n_kt, s);
     s = (int32_t)ceil_div(n_kt, per);
     int32_t base = -1;
+    const bool dec_tile = t.req >= np;
     if (s > 1) {
       base = n_partials;
       n_partials += s * kPrefillRows;
@@ -193,7 +202,7 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
           w.m_tasks.push_back((t.qrow0 + i) * hq + t.head + j);
           w.m_tasks.push_back(base + j * npos + i);
           w.m_tasks.push_back(kPrefillRows);
-          w.m_tasks.push_back(s);
+          w.m_tasks.push_back(s | (dec_tile ? 1 << 16 : 0));
         }
     }
     w.p_splits_max = std::max(w.p_splits_max, s);
@@ -203,7 +212,13 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
       PI it;
       it.f = {t.qrow0, t.head, t.nrows, t.pos0, kb, ke, t.req,
               base < 0 ? -1 : base + k * kPrefillRows};
-      it.work = double(t.nrows) * double(ke - kb);
+      // a wave computes its 64 rows whatever the valid count, so a one-row
+      // decode tile costs a full wave per head (batched prefill only; the
+      // tuned lists keep the valid-row estimate)
+      const double rows = dec_tile || decodes_as_prefill
+                              ? double(nh) * kWaveRows * ceil_div(t.nrows, kWaveRows)
+                              : double(t.nrows);
+      it.work = rows * double(ke - kb);
       pitems.push_back(std::move(it));
     }
   }
@@ -246,7 +261,7 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
   }
   struct DI { std::array<int32_t, D_FIELDS> f; int32_t work; };
   std::vector<DI> ditems;
-  for (int32_t i = 0; i < nd; ++i) {
+  for (int32_t i = 0; i < (decodes_as_prefill ? 0 : nd); ++i) {
     const int32_t kv = b.dkv[i];
     const int32_t steps = (int32_t)ceil_div(kv, kDecodeStep);
     int64_t s64 = force_d_splits > 0

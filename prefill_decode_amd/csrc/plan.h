@@ -138,9 +138,13 @@ int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu, int32_t sched_
 // decode requests are split until there are about `d_units_per_slot` units
 // per decode wavefront (chunks of at least kMinDecodeChunk keys, or
 // kMinDecodeChunkSmall when the batch has too few decode keys for that).
+// With `decodes_as_prefill` (the batched-prefill comparator) every decode
+// request becomes a one-row prefill tile per group of packed query heads
+// (P_KVREQ >= number of prefill requests marks it; its row is the decode
+// index) and no decode unit is made.
 void build_lists(const Batch& b, const pod_device_desc_t& dev,
                  int64_t prefill_slots, int32_t p_half_items_per_slot, int64_t decode_wave_slots,
                  int32_t d_units_per_slot, int32_t force_p_splits, int32_t force_d_splits,
-                 WorkLists* out);
+                 WorkLists* out, bool decodes_as_prefill = false);
 
 }  // namespace pod

@@ -37,8 +37,14 @@ def run_path(runner, path):
     runner.lse_decode.fill_(float("nan"))
     if path == "fused":
         runner.run()
-    else:
+    elif path == "seq":
         runner.sequential_run()
+    elif path == "streams":
+        runner.streams_run(torch.cuda.Stream())
+    elif path == "batched":
+        runner.batched_prefill_run()
+    else:
+        raise ValueError(path)
     torch.cuda.synchronize()
     return runner.outputs()
 

@@ -52,29 +52,52 @@ def test_fullsize_sampled(name):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", inputs.CONFIG_NAMES)
-def test_fullsize_every_row(name):
-    # every prefill row and decode of the full-size batch, both paths,
-    # against the fp64 oracle of the whole batch
+def _every_row(spec, paths, tunings=()):
     import torch
-    spec = inputs.config_spec(name)
-    say(f"[fullsize-all] {name}: generating on device")
+    say(f"[fullsize-all] {spec.name}: generating on device")
     bd = inputs.make_batch_device(spec, poison=True)
-    runner = B.BatchRunner(bd)
+    runner = B.BatchRunner(bd, B.make_tuning(flags=B.FLAG_BATCHED_PREFILL))
     host = inputs.host_subset(bd, list(range(spec.num_prefill)), list(range(spec.num_decode)))
     say("  oracle on the whole batch")
     ref = oracle.batch_attention(host)
     del host
-    for path in ("fused", "seq"):
+    for path in paths:
         say(f"  path {path}")
-        compare(run_path(runner, path), ref, f"{name}-all/{path}")
-    del runner, bd, ref
+        compare(run_path(runner, path), ref, f"{spec.name}-all/{path}")
+    del runner
+    for label, tun in tunings:
+        say(f"  fused, {label}")
+        r2 = B.BatchRunner(bd, tun)
+        compare(run_path(r2, "fused"), ref, f"{spec.name}-all/{label}")
+        del r2
+    del bd, ref
     torch.cuda.empty_cache()
 
 
-def _trace(spec, bd, mode):
+@pytest.mark.parametrize("name", inputs.CONFIG_NAMES)
+def test_fullsize_every_row(name):
+    # every prefill row and decode of the full-size batch, on the fused and
+    # sequential paths and the two comparators, against the fp64 oracle of
+    # the whole batch; the llama3-8b layer also under the co-location and
+    # ordered scheduler modes
+    tunings = ()
+    if name == "llama3_8b":
+        tunings = (("colocate", B.make_tuning(sched_mode=B.SCHED_COLOCATE)),
+                   ("ordered", B.make_tuning(sched_mode=B.SCHED_ORDERED)))
+    _every_row(inputs.config_spec(name), ("fused", "seq", "streams", "batched"), tunings)
+
+
+@pytest.mark.parametrize("n_dec", [32, 64, 128, 256])
+def test_fullsize_batched_sweep_every_row(n_dec):
+    # the batched mix's decode-count sweep, every row, both paths
+    _every_row(inputs.config_spec("batched", n_dec=n_dec), ("fused", "seq"))
+
+
+def _trace(spec, bd, mode, ref=None):
     runner = B.BatchRunner(bd, B.make_tuning(flags=B.FLAG_TRACE, sched_mode=mode))
-    run_path(runner, "fused")
+    got = run_path(runner, "fused")
+    if ref is not None:
+        compare(got, ref, f"trace mode {mode}")
     info = runner.plan.info()
     tr = runner.plan.read_trace()
     n_p, n_d = info["prefill_items"], info["decode_items"]
@@ -91,8 +114,11 @@ def test_scheduler_traces():
     spec = inputs.config_spec("llama3_8b")
     say("[trace] llama3_8b")
     bd = inputs.make_batch_device(spec)
+    host = inputs.host_subset(bd, list(range(spec.num_prefill)), list(range(spec.num_decode)))
+    ref = oracle.batch_attention(host)
+    del host
     # co-location on every CU: most CUs run a prefill and a decode unit at once
-    info, tr = _trace(spec, bd, B.SCHED_COLOCATE)
+    info, tr = _trace(spec, bd, B.SCHED_COLOCATE, ref)
     role, slot = tr[:, 2], tr[:, 1]
     both = 0
     slots = np.unique(slot)
@@ -108,7 +134,7 @@ def test_scheduler_traces():
     assert both >= 0.5 * len(slots)
     # CU partition (the default): about q/8 of the CUs start on prefill, and
     # the prefill and decode units overlap in time across the GPU
-    info, tr = _trace(spec, bd, B.SCHED_AUTO)
+    info, tr = _trace(spec, bd, B.SCHED_AUTO, ref)
     assert info["sched_mode"] == B.SCHED_SPLIT
     q = info["prefill_quarters_per_cu"]
     role, slot, t0, t1 = tr[:, 2], tr[:, 1], tr[:, 4], tr[:, 5]

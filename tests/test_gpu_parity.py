@@ -90,6 +90,26 @@ def test_forced_splits(ps, ds):
     _check(spec, B.make_tuning(prefill_kv_splits=ps, decode_kv_splits=ds))
 
 
+_SHARP_REF = {}
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 8, 16, 64])
+@pytest.mark.parametrize("which", [0, 1, 4], ids=["tiny", "llama3_8b_r", "batched_r"])
+def test_sharp_scale_forced_splits(which, splits):
+    # sm_scale = 1 (a peaked softmax, O = O(1)) with every split count the
+    # tuning accepts up to its cap, for prefill and decode at once: where a
+    # row's splits nearly cancel, the partials' precision shows
+    spec = inputs.with_scale(reduced_specs()[which], 1.0)
+    say(f"[sharp-splits] {spec.name} splits {splits}")
+    if spec.name not in _SHARP_REF:
+        b = inputs.make_batch_host(spec, poison=True)
+        _SHARP_REF[spec.name] = (b, oracle.batch_attention(b))
+    b, ref = _SHARP_REF[spec.name]
+    runner = B.BatchRunner(b, B.make_tuning(prefill_kv_splits=splits, decode_kv_splits=splits))
+    for path in ("fused", "seq"):
+        compare(run_path(runner, path), ref, f"{spec.name}/splits{splits}/{path}")
+
+
 def test_fused_equals_matched_sequential_bitwise_and_sched_modes():
     spec = reduced_specs()[4]
     b = inputs.make_batch_host(spec)

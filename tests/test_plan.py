@@ -274,3 +274,59 @@ def test_decode_chunk_floor_follows_batch_size():
         d = D[D[:, 0] == i]
         n_split = len(d) // spec.num_kv_heads
         assert n_split <= -(-kv // 512), (i, kv, n_split)
+
+
+@pytest.mark.parametrize("spec", [s for s in _specs() if s.name != "empty"], ids=lambda s: s.name)
+def test_batched_prefill_lists_cover_every_row(spec):
+    # the batched-prefill comparator's list: prefill tiles as in the other
+    # lists, plus one one-row tile per (decode, packed head group) whose KV
+    # splits partition the decode's keys; merge tasks write the decode rows
+    import dataclasses
+    pl = _spec_lists(spec, flags=B.FLAG_BATCHED_PREFILL)
+    n_p = spec.num_prefill
+    hq, g = spec.num_qo_heads, spec.num_qo_heads // spec.num_kv_heads
+    nh = 4 if g % 4 == 0 else 2 if g % 2 == 0 else 1
+    P = pl.export(8).reshape(-1, P_F)
+    M = pl.export(9).reshape(-1, M_F)
+    po = pl.export(10)
+    assert po[0] == 0 and po[-1] == len(P) and np.all(np.diff(po) >= 0)
+    is_dec = P[:, 6] >= n_p
+    m_dec = (M[:, 3] >> 16) == 1
+    # the prefill tiles (and their merge tasks) pass the tuned lists' checks
+    _check_lists(dataclasses.replace(spec, decode_kv_len=()), P[~is_dec].ravel(),
+                 np.zeros(0, np.int32), M[~m_dec].ravel(), [0, int((~is_dec).sum())],
+                 pl.info()["num_partials"])
+    cov = np.zeros((spec.num_decode, hq), np.int32)
+    tiles = {}
+    for it in P[is_dec]:
+        i, h = int(it[0]), int(it[1])
+        assert int(it[6]) == n_p + i and int(it[2]) == 1
+        assert int(it[3]) == spec.decode_kv_len[i] - 1     # the decode row's position
+        tiles.setdefault((i, h), []).append(it)
+    used = set()
+    for (i, h), its in tiles.items():
+        assert h % nh == 0
+        cov[i, h:h + nh] += 1
+        its = sorted(its, key=lambda x: x[4])
+        assert int(its[0][4]) == 0 and int(its[-1][5]) == spec.decode_kv_len[i]
+        for a, b in zip(its[:-1], its[1:]):
+            assert int(a[5]) == int(b[4])
+        if len(its) == 1:
+            assert int(its[0][7]) == -1
+        else:
+            for t in its:
+                for j in range(nh):
+                    slot = int(t[7]) + j * (256 // nh)
+                    assert slot not in used
+                    used.add(slot)
+    assert np.all(cov == 1)
+    # decode merge tasks: one per split (decode, head), reading exactly the
+    # slots the decode tiles write, and writing decode rows
+    outs = set()
+    for t in M[m_dec]:
+        out, base, stride, n = int(t[0]), int(t[1]), int(t[2]), int(t[3]) & 0xFFFF
+        assert 0 <= out < spec.num_decode * hq and out not in outs
+        outs.add(out)
+        for k in range(n):
+            used.remove(base + k * stride)
+    assert not used
