@@ -1,6 +1,7 @@
 """Benchmark: fused prefill+decode attention of one hybrid batch on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-flush] [--no-cpu]
+                    [--no-per-config] [--config-steps K2]
     python bench.py --pmc-run [--config NAME]          (driver for rocprofv3 counter runs)
     python bench.py --summarize-pmc DIR [--config NAME] (writes profiles/traffic_*.md)
     python bench.py --summarize-stats DIR [--config NAME] (writes profiles/*_stats.md)
@@ -14,8 +15,17 @@ streams its KV cache from HBM; the write is outside the events.  HIP events
 are recorded on the stream the kernels run on: around the whole step, and
 (through pod_attn_run_events) immediately around the fused kernel, whose time
 the roofline object uses.  The sequential baseline (prefill kernel, decode
-kernel, merge; its own plan) is timed the same way in the same run.  The fp64
-CPU oracle is timed on the host cores on a bounded sample of the batch.
+kernel, merge; its own plan) and the pages' comparators (the two kernels on
+two streams; every request through the prefill kernel; a persistent launch
+over one prefill-then-decode queue) are timed the same way in the same run,
+interleaved step by step with the fused path.  The fp64 CPU oracle is timed on
+the host cores on a bounded sample of the batch.
+
+The headline workload (default: the 70B-shaped layer at TP = 1, the largest
+single-GPU configuration) is timed for exactly --steps steps per path; every
+other workload and the batched mix's decode-count sweep follow in
+`per_config` with --config-steps steps each.  A streaming-read probe over a
+4 GiB buffer gives the attainable HBM read rate (`hbm_read_ceiling`).
 
 Prints one JSON line.
 """
@@ -335,15 +345,171 @@ Commands (from the repository root; `$D` = a scratch directory):
     print(txt)
 
 
+PATHS = ("fused", "seq", "streams", "batched", "ordered")
+PATH_NAMES = {
+    "fused": "pod_attn_run: one fused launch (+ merge)",
+    "seq": "pod_attn_sequential_run: prefill kernel, decode kernel, merge on one stream",
+    "streams": "pod_attn_streams_run: prefill and decode kernels on two streams, merge",
+    "batched": "pod_attn_batched_prefill_run: every request through the prefill kernel "
+               "(decodes as one-row chunks), merge",
+    "ordered": "pod_attn_run with the ordered scheduler: one persistent launch over a unified "
+               "queue, prefill units first",
+}
+
+
+class Timer:
+    """Events recorded on the stream the kernels run on, with a cache-evicting
+    1 GiB fill before each timed call (outside the events)."""
+
+    def __init__(self, torch, flush):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+        self.flush = flush
+        self.buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
+        self.n = 0
+
+    def ev(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def evict(self):
+        if self.buf is not None:
+            self.n += 1
+            self.buf.fill_(self.n & 0xFF)
+
+    def interleaved(self, calls, steps, warmup):
+        """Median-ready times (ms) of each named call, the calls interleaved
+        step by step so that drift hits them alike."""
+        for _ in range(warmup):
+            for f in calls.values():
+                f()
+        self.torch.cuda.synchronize()
+        evs = {k: [(self.ev(), self.ev()) for _ in range(steps)] for k in calls}
+        wall0 = time.perf_counter()
+        for i in range(steps):
+            for k, f in calls.items():
+                self.evict()
+                evs[k][i][0].record(self.stream)
+                f()
+                evs[k][i][1].record(self.stream)
+        self.torch.cuda.synchronize()
+        self.last_wall = time.perf_counter() - wall0
+        return {k: np.array([a.elapsed_time(b) for a, b in v]) for k, v in evs.items()}
+
+    def fused_kernel(self, runner, steps):
+        """The fused kernel alone: events recorded by pod_attn_run_events
+        immediately around its launch."""
+        kv = [(self.ev(), self.ev()) for _ in range(steps)]
+        for a, b in kv:
+            self.evict()
+            runner.run_events(a, b)
+        self.torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in kv])
+
+
+def read_ceiling(torch, B, timer, reps=5, gib=4):
+    """Attainable HBM read rate: the library's streaming-read probe over a
+    4 GiB buffer (the 256 MB Infinity Cache can hold under 7% of it), median
+    of `reps` reads."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda").fill_(3)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    best = {}
+    for blocks in (512, 1024, 2048):
+        B.probe_read_bw(buf, sink, blocks)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = timer.ev(), timer.ev()
+            a.record(timer.stream)
+            B.probe_read_bw(buf, sink, blocks)
+            b.record(timer.stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        best[blocks] = buf.numel() / (float(np.median(ts)) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    k = max(best, key=best.get)
+    return {"gbs": best[k], "probe_blocks": k, "bytes": gib << 30, "reps": reps,
+            "by_blocks": {str(b): round(v, 1) for b, v in best.items()}}
+
+
+def pct(a, q):
+    return float(np.percentile(a, q)) * 1e3
+
+
+def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup, tuning_kw,
+                   paths=PATHS):
+    """Times every path on one workload; returns (runner, fields)."""
+    spec = inputs.config_spec(name, n_dec=n_dec)
+    batch = inputs.make_batch_device(spec)
+    counts = metrics.algorithmic_counts(spec)
+    flags = B.FLAG_BATCHED_PREFILL if "batched" in paths else 0
+    t0 = time.perf_counter()
+    runner = B.BatchRunner(batch, B.make_tuning(flags=flags, **tuning_kw))
+    torch.cuda.synchronize()
+    plan_first_ms = (time.perf_counter() - t0) * 1e3
+    # warm host planning alone (no device work, no allocation on the device)
+    warm = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        p = B.plan_host(runner.params, spec.prefill_qo_len, spec.prefill_kv_len,
+                        spec.decode_kv_len, B.make_tuning(**tuning_kw))
+        warm.append((time.perf_counter() - t0) * 1e3)
+        p.destroy()
+    calls = {"fused": runner.run, "seq": runner.sequential_run}
+    side = torch.cuda.Stream()
+    if "streams" in paths:
+        calls["streams"] = lambda: runner.streams_run(side)
+    if "batched" in paths:
+        calls["batched"] = runner.batched_prefill_run
+    ordered = None
+    if "ordered" in paths:
+        ordered = B.BatchRunner(batch, B.make_tuning(sched_mode=B.SCHED_ORDERED))
+        calls["ordered"] = ordered.run
+    t = timer.interleaved(calls, steps, warmup)
+    kern = timer.fused_kernel(runner, steps)
+    med = {k: float(np.median(v)) * 1e-3 for k, v in t.items()}
+    t_step, t_kern = med["fused"], float(np.median(kern)) * 1e-3
+    roof_s = metrics.overlap_roofline_s(counts)
+    info = runner.plan.info()
+    f = {
+        "workload": DESCR.get(name, spec.name),
+        "fused_us": t_step * 1e6,
+        "fused_us_p10_p90": [pct(t["fused"], 10), pct(t["fused"], 90)],
+        "fused_kernel_us": t_kern * 1e6,
+        "sequential_us": med["seq"] * 1e6,
+        "sequential_us_p10_p90": [pct(t["seq"], 10), pct(t["seq"], 90)],
+        "speedup_vs_sequential": med["seq"] / t_step,
+        "comparators_us": {k: med[k] * 1e6 for k in ("streams", "batched", "ordered") if k in med},
+        "overlap_roofline_us": roof_s * 1e6,
+        "overlap_roofline_frac_step": roof_s / t_step,
+        "overlap_roofline_frac_kernel": roof_s / t_kern,
+        "achieved_tflops": counts["flops"] / t_step / 1e12,
+        "achieved_hbm_gbs": counts["bytes"] / t_step / 1e9,
+        "algorithmic": {"gflop": counts["flops"] / 1e9, "gbytes": counts["bytes"] / 1e9},
+        "traffic_bytes_per_launch": read_traffic(spec.name) if n_dec is None else None,
+        "plan": {"first_call_ms": plan_first_ms, "host_warm_ms": float(np.median(warm)),
+                 "prefill_items": info["prefill_items"], "decode_items": info["decode_items"],
+                 "merge_tasks": info["merge_tasks"],
+                 "prefill_quarters_per_cu": info["prefill_quarters_per_cu"],
+                 "sched_mode": info["sched_mode"]},
+    }
+    del ordered
+    return runner, batch, spec, counts, t, kern, f
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="llama3_8b")
+    ap.add_argument("--config", default="l70b_tp1")
     ap.add_argument("--n-dec", type=int, default=None, help="batched: decode-count sweep point")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time the headline workload only")
+    ap.add_argument("--config-steps", type=int, default=10,
+                    help="timed steps per path for the other workloads")
     ap.add_argument("--quarters", type=int, default=-1, help="prefill quarters per CU (-1 auto)")
     ap.add_argument("--prefill-splits", type=int, default=0, help="force prefill KV splits (0 auto)")
     ap.add_argument("--decode-splits", type=int, default=0, help="force decode KV splits (0 auto)")
@@ -374,70 +540,26 @@ def main():
     from prefill_decode_amd import inputs, metrics
 
     torch.cuda.set_device(0)
-    spec = inputs.config_spec(args.config, n_dec=args.n_dec)
-    batch = inputs.make_batch_device(spec)
-    counts = metrics.algorithmic_counts(spec)
-    tuning = B.make_tuning(prefill_quarters_per_cu=args.quarters, sched_mode=args.sched,
-                           prefill_kv_splits=args.prefill_splits, decode_kv_splits=args.decode_splits)
-    t0 = time.perf_counter()
-    runner = B.BatchRunner(batch, tuning)
-    torch.cuda.synchronize()
-    plan_ms = (time.perf_counter() - t0) * 1e3
-    info = runner.plan.info()
-    stream = torch.cuda.current_stream()
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-
-    def do_flush(i):
-        if not args.no_flush:
-            flush.fill_(i & 0xFF)
-
-    def new_ev():
-        return torch.cuda.Event(enable_timing=True)
-
-    for i in range(args.warmup):
-        runner.run()
-        runner.sequential_run()
-    torch.cuda.synchronize()
-
-    # timed steps: pod_attn_run and pod_attn_sequential_run, each after a
-    # cache-evicting fill, with events only around the whole step
-    ev = [[new_ev() for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(args.steps):
-        e = ev[i]
-        do_flush(2 * i)
-        e[0].record(stream)
-        runner.run()
-        e[1].record(stream)
-        do_flush(2 * i + 1)
-        e[2].record(stream)
-        runner.sequential_run()
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    step_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    seq_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
-    # the fused kernel alone (events recorded around its launch)
-    kv = [[new_ev() for _ in range(2)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        do_flush(i)
-        runner.run_events(kv[i][0], kv[i][1])
-    torch.cuda.synchronize()
-    fused_ms = np.array([e[0].elapsed_time(e[1]) for e in kv])
-    # warm (no flush) back-to-back
-    w0, w1 = new_ev(), new_ev()
-    w0.record(stream)
+    timer = Timer(torch, not args.no_flush)
+    tuning_kw = dict(prefill_quarters_per_cu=args.quarters, sched_mode=args.sched,
+                     prefill_kv_splits=args.prefill_splits, decode_kv_splits=args.decode_splits)
+    # ---- the headline workload: exactly --steps timed steps per path ----
+    print(f"bench: {args.config} ({args.steps} steps, {args.warmup} warm-up)", file=sys.stderr,
+          flush=True)
+    runner, batch, spec, counts, t, kern, head = measure_config(
+        torch, B, inputs, metrics, timer, args.config, args.n_dec, args.steps, args.warmup,
+        tuning_kw)
+    wall = timer.last_wall
+    # warm (no eviction) back-to-back fused steps
+    w0, w1 = timer.ev(), timer.ev()
+    w0.record(timer.stream)
     for _ in range(args.steps):
         runner.run()
-    w1.record(stream)
+    w1.record(timer.stream)
     torch.cuda.synchronize()
     warm_ms = w0.elapsed_time(w1) / args.steps
 
-    t_step = float(np.median(step_ms)) * 1e-3
-    t_kern = float(np.median(fused_ms)) * 1e-3
-    t_seq = float(np.median(seq_ms)) * 1e-3
-    roof_s = metrics.overlap_roofline_s(counts)
+    t_step, t_kern = head["fused_us"] * 1e-6, head["fused_kernel_us"] * 1e-6
     hbm_bound = counts["bytes"] / metrics.PEAK_HBM_BYTES >= counts["flops"] / metrics.PEAK_BF16_FLOPS
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": counts["bytes"] / t_kern / 1e9,
@@ -446,7 +568,7 @@ def main():
         roof = {"bound": "mfma", "achieved": counts["flops"] / t_kern / 1e12,
                 "peak": metrics.PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = read_traffic(args.config) if args.n_dec is None else None
+    roof["traffic"] = head["traffic_bytes_per_launch"]
     roof["kernel"] = "pod_fused_kernel"
     roof["kernel_us"] = t_kern * 1e6
 
@@ -463,28 +585,45 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": DESCR.get(args.config, spec.name), "name": spec.name,
+        "config": {"workload": head["workload"], "name": spec.name,
                    "num_prefill": spec.num_prefill, "num_decode": spec.num_decode,
                    "cache_flush": not args.no_flush},
-        "overlap_roofline_us": roof_s * 1e6,
-        "overlap_roofline_frac": roof_s / t_step,
-        "sequential_us": t_seq * 1e6,
-        "speedup_vs_sequential": t_seq / t_step,
-        "step_us_p10_p90": [float(np.percentile(step_ms, 10)) * 1e3,
-                            float(np.percentile(step_ms, 90)) * 1e3],
-        "sequential_us_p10_p90": [float(np.percentile(seq_ms, 10)) * 1e3,
-                                  float(np.percentile(seq_ms, 90)) * 1e3],
+        "overlap_roofline_us": head["overlap_roofline_us"],
+        "overlap_roofline_frac": head["overlap_roofline_frac_step"],
+        "sequential_us": head["sequential_us"],
+        "speedup_vs_sequential": head["speedup_vs_sequential"],
+        "step_us_p10_p90": head["fused_us_p10_p90"],
+        "sequential_us_p10_p90": head["sequential_us_p10_p90"],
+        "comparators_us": head["comparators_us"],
+        "comparator_paths": PATH_NAMES,
         "warm_cache_step_us": warm_ms * 1e3,
-        "achieved_tflops": counts["flops"] / t_step / 1e12,
-        "achieved_hbm_gbs": counts["bytes"] / t_step / 1e9,
-        "algorithmic": {"gflop": counts["flops"] / 1e9, "gbytes": counts["bytes"] / 1e9},
-        "plan": {"host_ms": plan_ms, "prefill_items": info["prefill_items"],
-                 "decode_items": info["decode_items"], "merge_tasks": info["merge_tasks"],
-                 "prefill_quarters_per_cu": info["prefill_quarters_per_cu"],
-                 "sched_mode": info["sched_mode"]},
+        "achieved_tflops": head["achieved_tflops"],
+        "achieved_hbm_gbs": head["achieved_hbm_gbs"],
+        "algorithmic": head["algorithmic"],
+        "plan": head["plan"],
         "wall_s_timed_loop": wall,
         "roofline": roof,
     }
+    del runner
+    torch.cuda.empty_cache()
+    out["hbm_read_ceiling"] = read_ceiling(torch, B, timer)
+    out["roofline"]["frac_of_read_ceiling"] = roof["achieved"] / out["hbm_read_ceiling"]["gbs"] \
+        if hbm_bound else None
+    if not args.no_per_config:
+        per = {}
+        todo = [(n, None) for n in inputs.CONFIG_NAMES] + [("batched", n) for n in (32, 64, 128, 256)]
+        for name, nd in todo:
+            key = name if nd is None else f"batched_d{nd}"
+            if name == args.config and nd == args.n_dec:
+                per[key] = head
+                continue
+            print(f"bench: {key}", file=sys.stderr, flush=True)
+            r, *_rest, f = measure_config(torch, B, inputs, metrics, timer, name, nd,
+                                          args.config_steps, 2, tuning_kw)
+            per[key] = f
+            del r, _rest
+            torch.cuda.empty_cache()
+        out["per_config"] = per
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(batch, spec)
     print(json.dumps(out), flush=True)

@@ -326,6 +326,16 @@ const char* pod_attn_last_error(void);
  * [2 * num_blocks]).  Used to check the per-CU slot map on a device. */
 pod_status_t pod_attn_probe_hwid(int32_t num_blocks, int32_t* out, hipStream_t stream);
 
+/* HBM read-rate probe (measurement aid, not part of attention): launches
+ * `num_blocks` workgroups of 256 threads that read bytes / 16 16-byte words
+ * of `buf` (device, 16-byte aligned) once each with non-temporal loads and
+ * write nothing, except to `sink` (device uint32) in the unlikely case that
+ * the folded data equals a fixed constant.  Timing it with events on
+ * `stream` gives the device's attainable read rate beside the datasheet
+ * peak.  Errors: POD_ERR_INVALID_ARGUMENT, POD_ERR_HIP. */
+pod_status_t pod_attn_probe_read_bw(const void* buf, size_t bytes, uint32_t* sink,
+                                    int32_t num_blocks, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

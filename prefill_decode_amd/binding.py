@@ -14,7 +14,10 @@ from typing import Dict, Optional, Sequence
 
 import numpy as np
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpod_attn.so")
+# POD_ATTN_LIB selects another build of the same library (the host-sanitizer
+# build in the tests); by default the in-tree build is loaded.
+_LIB_PATH = os.environ.get("POD_ATTN_LIB") or \
+    os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpod_attn.so")
 _lib = None
 
 POD_OK = 0
@@ -30,7 +33,8 @@ EXPORTED = ("pod_attn_plan", "pod_attn_plan_host", "pod_attn_run", "pod_attn_run
             "pod_attn_sequential_run", "pod_attn_streams_run", "pod_attn_batched_prefill_run",
             "pod_attn_merge",
             "pod_attn_plan_info", "pod_attn_plan_export", "pod_attn_read_trace",
-            "pod_attn_plan_destroy", "pod_attn_last_error", "pod_attn_probe_hwid")
+            "pod_attn_plan_destroy", "pod_attn_last_error", "pod_attn_probe_hwid",
+            "pod_attn_probe_read_bw")
 
 
 class PodError(RuntimeError):
@@ -116,6 +120,8 @@ def lib():
         L.pod_attn_plan_destroy.restype = None
         L.pod_attn_last_error.restype = C.c_char_p
         L.pod_attn_probe_hwid.argtypes = [C.c_int32, C.c_void_p, C.c_void_p]
+        L.pod_attn_probe_read_bw.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32,
+                                             C.c_void_p]
         for name in EXPORTED:
             if name not in ("pod_attn_plan_destroy", "pod_attn_last_error"):
                 getattr(L, name).restype = C.c_int
@@ -304,6 +310,13 @@ def probe_hwid(num_blocks: int, device="cuda", stream=None) -> np.ndarray:
     _check(lib().pod_attn_probe_hwid(num_blocks, C.c_void_p(out.data_ptr()), _stream(stream)))
     torch.cuda.synchronize()
     return out.cpu().numpy().reshape(-1, 2)
+
+
+def probe_read_bw(buf, sink, num_blocks=2048, stream=None):
+    """Enqueues one read of the whole device tensor `buf` (the HBM read-rate
+    probe); `sink` is a device uint32/int32 tensor of at least one element."""
+    _check(lib().pod_attn_probe_read_bw(_dp(buf), buf.numel() * buf.element_size(), _dp(sink),
+                                        int(num_blocks), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

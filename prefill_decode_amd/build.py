@@ -68,5 +68,34 @@ def build(verbose: bool = True, save_isa: bool = False) -> str:
     return LIB
 
 
+# Host-side sanitizer build: the planner and the C ABI (host C++ only) are
+# compiled with AddressSanitizer and UndefinedBehaviorSanitizer by g++ and
+# linked with the regular device-code object.  Loaded into a Python process
+# that preloads the gcc ASan runtime (see tests/test_sanitizers.py).
+SAN_DIR = os.path.join(BUILD, "sanitize")
+SAN_LIB = os.path.join(SAN_DIR, "libpod_attn.so")
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=undefined"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Builds _build/sanitize/libpod_attn.so (host code instrumented); returns its path."""
+    kern_obj = os.path.join(BUILD, "kernels.o")
+    if not os.path.exists(kern_obj):
+        build(verbose)
+    os.makedirs(SAN_DIR, exist_ok=True)
+    cxx = shutil.which("g++") or "g++"
+    objs = [kern_obj]
+    for src in ("api.cpp", "plan.cpp"):
+        obj = os.path.join(SAN_DIR, src.replace(".cpp", ".o"))
+        _run([cxx, *CXX_FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    _run([cxx, "-shared", "-fPIC", *SAN_FLAGS, *objs, "-o", SAN_LIB,
+          f"-L{ROCM}/lib", "-lamdhip64", f"-Wl,-rpath,{ROCM}/lib"], verbose)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True, save_isa="--isa" in sys.argv)
+    if "--sanitize" in sys.argv:
+        build_sanitized(verbose=True)

@@ -95,13 +95,20 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   const int64_t slots = (int64_t)dev.num_cus * c.wgs_per_cu;
   const int64_t p_slots_coloc = std::max<int64_t>(1, (int64_t)dev.num_cus * c.prefill_quarters / 4);
   const bool small_prefill = sum_qo <= 1536;
-  const int64_t fused_p_slots = small_prefill ? p_slots_coloc : slots;
-  const int64_t fused_d_waves =
-      std::max<int64_t>(kWavesPerWG, (int64_t)dev.num_cus * (4 * c.wgs_per_cu - c.prefill_quarters));
-  const int32_t p_half_items =
-      small_prefill ? kFusedPrefillHalfItemsPerSlotSmall : kFusedPrefillHalfItemsPerSlotLarge;
-  build_lists(pl->batch, dev, fused_p_slots, p_half_items, fused_d_waves, kFusedDecodeUnitsPerWave,
-              t.prefill_kv_splits, t.decode_kv_splits, &pl->fused);
+  if (c.sched_mode == POD_SCHED_ORDERED) {
+    // one queue, prefill units first: each part has the whole GPU in turn,
+    // so the lists are sized as the sequential kernels' are
+    build_lists(pl->batch, dev, slots, kSeqPrefillHalfItemsPerSlot, slots * kWavesPerWG,
+                kSeqDecodeUnitsPerWave, t.prefill_kv_splits, t.decode_kv_splits, &pl->fused);
+  } else {
+    const int64_t fused_p_slots = small_prefill ? p_slots_coloc : slots;
+    const int64_t fused_d_waves = std::max<int64_t>(
+        kWavesPerWG, (int64_t)dev.num_cus * (4 * c.wgs_per_cu - c.prefill_quarters));
+    const int32_t p_half_items =
+        small_prefill ? kFusedPrefillHalfItemsPerSlotSmall : kFusedPrefillHalfItemsPerSlotLarge;
+    build_lists(pl->batch, dev, fused_p_slots, p_half_items, fused_d_waves,
+                kFusedDecodeUnitsPerWave, t.prefill_kv_splits, t.decode_kv_splits, &pl->fused);
+  }
   // Sequential plan: each kernel has the whole GPU.
   pl->seq_is_fused = t.match_sequential == 1;
   if (!pl->seq_is_fused)
@@ -572,6 +579,14 @@ pod_status_t pod_attn_probe_hwid(int32_t num_blocks, int32_t* out, hipStream_t s
   if (num_blocks < 1 || !out) return set_err(POD_ERR_INVALID_ARGUMENT, "bad probe arguments");
   hipError_t e = launch_probe(out, num_blocks, stream);
   return e == hipSuccess ? POD_OK : hip_err(e, "probe kernel launch");
+}
+
+pod_status_t pod_attn_probe_read_bw(const void* buf, size_t bytes, uint32_t* sink,
+                                    int32_t num_blocks, hipStream_t stream) {
+  if (!buf || !sink || num_blocks < 1 || bytes < 16 || !aligned16(buf))
+    return set_err(POD_ERR_INVALID_ARGUMENT, "bad read-probe arguments");
+  hipError_t e = launch_read_probe(buf, (int64_t)(bytes / 16), 0x9E3779B9u, sink, num_blocks, stream);
+  return e == hipSuccess ? POD_OK : hip_err(e, "read-probe kernel launch");
 }
 
 }  // extern "C"

@@ -86,5 +86,7 @@ hipError_t launch_prefill(const KernelArgs& a, int kv_mode, int grid, hipStream_
 hipError_t launch_decode(const KernelArgs& a, int kv_mode, int grid, hipStream_t s);
 hipError_t launch_merge(const KernelArgs& a, int grid, hipStream_t s);
 hipError_t launch_probe(int32_t* out, int blocks, hipStream_t s);
+hipError_t launch_read_probe(const void* buf, int64_t n16, uint32_t never, uint32_t* sink,
+                             int blocks, hipStream_t s);
 
 }  // namespace pod

@@ -1237,6 +1237,33 @@ __global__ __launch_bounds__(256) void pod_merge_kernel(KernelArgs a) {
   if (j == 0 && lse) lse[out] = tot > 0.0f ? (m + log2_(tot)) * kLn2 : kNegInf;
 }
 
+// HBM read-rate probe: workgroup b streams the contiguous chunk b of the
+// buffer (so each walks its own pages in order), every lane with eight
+// 16-byte non-temporal loads in flight, and folds the data into one word that
+// is stored only if it matches `never` (no load is dead code, nothing is
+// written).
+__global__ __launch_bounds__(256) void pod_read_probe_kernel(const u32x4* __restrict__ p,
+                                                             int64_t n16, uint32_t never,
+                                                             uint32_t* sink) {
+  const int64_t chunk = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * chunk;
+  const int64_t hi = min(n16, lo + chunk);
+  int64_t i = lo + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 7 * 256 < hi; i += 8 * 256) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < hi; i += 256) {
+    const u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  if (acc == never) sink[0] = acc;
+}
+
 __global__ void pod_probe_kernel(int32_t* out) {
   if (threadIdx.x == 0) {
     out[2 * blockIdx.x] = (int32_t)__builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4);
@@ -1293,6 +1320,13 @@ hipError_t launch_decode(const KernelArgs& a, int kv_mode, int grid, hipStream_t
 
 hipError_t launch_merge(const KernelArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL(pod_merge_kernel, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void* buf, int64_t n16, uint32_t never, uint32_t* sink,
+                             int blocks, hipStream_t s) {
+  hipLaunchKernelGGL(pod_read_probe_kernel, dim3(blocks), dim3(256), 0, s, (const u32x4*)buf, n16,
+                     never, sink);
   return hipGetLastError();
 }
 
