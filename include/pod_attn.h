@@ -231,6 +231,29 @@ pod_status_t pod_attn_plan_host(const pod_attn_params_t* params,
                                 const pod_device_desc_t* device,
                                 pod_attn_plan_t* out_plan);
 
+/* pod_attn_plan for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the plan's workspace is a static 128 MiB device array of the library, one
+ * per device, held until the process ends; the caller passes no workspace.
+ * Arguments, validation and the returned plan are those of pod_attn_plan
+ * (runs use it with pod_attn_run / pod_attn_sequential_run / ... as usual).
+ * Allocates no device memory (no hipMalloc, hipFree or allocating library
+ * routine; the plan object itself is host memory, freed by
+ * pod_attn_plan_destroy).  The scratch is shared by every such plan on the
+ * device: a new pod_attn_plan_scratch call overwrites the work lists and
+ * counters of the previous one, so only the most recent scratch plan of a
+ * device may run, and runs that overlap in time race.  The counters are
+ * zeroed on `stream` by each call.
+ * Errors: those of pod_attn_plan; POD_ERR_WORKSPACE_TOO_SMALL (with the
+ * needed size) when the plan needs more than 128 MiB; POD_ERR_HIP when the
+ * scratch address cannot be obtained. */
+pod_status_t pod_attn_plan_scratch(const pod_attn_params_t* params,
+                                   int32_t num_prefill, const int32_t* prefill_qo_len,
+                                   const int32_t* prefill_kv_len,
+                                   int32_t num_decode, const int32_t* decode_kv_len,
+                                   const pod_attn_tuning_t* tuning, hipStream_t stream,
+                                   pod_attn_plan_t* out_plan);
+
 /* Fused run: one persistent kernel (two workgroups per CU) for all prefill
  * tiles and decode splits, then the merge kernel if any split exists.
  * Asynchronous on `stream`.

@@ -34,7 +34,7 @@ EXPORTED = ("pod_attn_plan", "pod_attn_plan_host", "pod_attn_run", "pod_attn_run
             "pod_attn_merge",
             "pod_attn_plan_info", "pod_attn_plan_export", "pod_attn_read_trace",
             "pod_attn_plan_destroy", "pod_attn_last_error", "pod_attn_probe_hwid",
-            "pod_attn_probe_read_bw")
+            "pod_attn_probe_read_bw", "pod_attn_plan_scratch")
 
 
 class PodError(RuntimeError):
@@ -99,6 +99,9 @@ def lib():
         L.pod_attn_plan.argtypes = [C.POINTER(Params), C.c_int32, i32p, i32p, C.c_int32, i32p,
                                     C.POINTER(Tuning), C.c_void_p, C.c_size_t,
                                     C.POINTER(C.c_size_t), C.c_void_p, C.POINTER(C.c_void_p)]
+        L.pod_attn_plan_scratch.argtypes = [C.POINTER(Params), C.c_int32, i32p, i32p,
+                                            C.c_int32, i32p, C.POINTER(Tuning), C.c_void_p,
+                                            C.POINTER(C.c_void_p)]
         L.pod_attn_plan_host.argtypes = [C.POINTER(Params), C.c_int32, i32p, i32p, C.c_int32,
                                          i32p, C.POINTER(Tuning), C.POINTER(DeviceDesc),
                                          C.POINTER(C.c_void_p)]
@@ -246,6 +249,19 @@ def plan(params: Params, prefill_qo: Sequence[int], prefill_kv: Sequence[int],
                                tp, C.c_void_p(ws.data_ptr()), ws.numel(), C.byref(need), s,
                                C.byref(h)))
     return Plan(h.value, workspace=ws)
+
+
+def plan_scratch(params: Params, prefill_qo: Sequence[int], prefill_kv: Sequence[int],
+                 decode_kv: Sequence[int], tuning: Optional[Tuning] = None,
+                 stream=None) -> Plan:
+    """Plans for the current device into the library's static scratch (no
+    device allocation; see pod_attn_plan_scratch for the sharing rules)."""
+    qo, kv, dk = _i32(prefill_qo), _i32(prefill_kv), _i32(decode_kv)
+    h = C.c_void_p(0)
+    _check(lib().pod_attn_plan_scratch(C.byref(params), len(qo), _ptr(qo), _ptr(kv), len(dk),
+                                       _ptr(dk), C.byref(tuning) if tuning else None,
+                                       _stream(stream), C.byref(h)))
+    return Plan(h.value)
 
 
 def _dp(t):

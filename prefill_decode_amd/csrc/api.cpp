@@ -385,6 +385,34 @@ pod_status_t pod_attn_plan(const pod_attn_params_t* params, int32_t num_prefill,
   return POD_OK;
 }
 
+pod_status_t pod_attn_plan_scratch(const pod_attn_params_t* params, int32_t num_prefill,
+                                   const int32_t* prefill_qo_len, const int32_t* prefill_kv_len,
+                                   int32_t num_decode, const int32_t* decode_kv_len,
+                                   const pod_attn_tuning_t* tuning, hipStream_t stream,
+                                   pod_attn_plan_t* out_plan) {
+  if (!out_plan) return set_err(POD_ERR_INVALID_ARGUMENT, "out_plan is NULL");
+  *out_plan = nullptr;
+  int device = -1;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return hip_err(e, "hipGetDevice");
+  void* ws = nullptr;
+  if ((e = scratch_address(device, &ws)) != hipSuccess)
+    return hip_err(e, "hipGetSymbolAddress(scratch)");
+  size_t need = 0;
+  pod_status_t st = pod_attn_plan(params, num_prefill, prefill_qo_len, prefill_kv_len, num_decode,
+                                  decode_kv_len, tuning, nullptr, 0, &need, stream, nullptr);
+  if (st != POD_OK) return st;
+  if (need > kScratchBytes) {
+    char buf[200];
+    std::snprintf(buf, sizeof(buf),
+                  "plan needs %zu bytes of workspace; the static scratch holds %zu (use "
+                  "pod_attn_plan with a caller workspace)", need, kScratchBytes);
+    return set_err(POD_ERR_WORKSPACE_TOO_SMALL, buf);
+  }
+  return pod_attn_plan(params, num_prefill, prefill_qo_len, prefill_kv_len, num_decode,
+                       decode_kv_len, tuning, ws, kScratchBytes, &need, stream, out_plan);
+}
+
 pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t,
                                  hipStream_t stream, hipEvent_t before_fused,
                                  hipEvent_t after_fused) {

@@ -86,6 +86,12 @@ hipError_t launch_prefill(const KernelArgs& a, int kv_mode, int grid, hipStream_
 hipError_t launch_decode(const KernelArgs& a, int kv_mode, int grid, hipStream_t s);
 hipError_t launch_merge(const KernelArgs& a, int grid, hipStream_t s);
 hipError_t launch_probe(int32_t* out, int blocks, hipStream_t s);
+
+// Size of the per-device static scratch (pod_attn_plan_scratch), and its
+// device address on `device` (which must be the current device on the first
+// call for it).
+constexpr size_t kScratchBytes = size_t(128) << 20;
+hipError_t scratch_address(int device, void** out);
 hipError_t launch_read_probe(const void* buf, int64_t n16, uint32_t never, uint32_t* sink,
                              int blocks, hipStream_t s);
 

@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "kernel_args.h"
@@ -1269,6 +1270,32 @@ __global__ void pod_probe_kernel(int32_t* out) {
     out[2 * blockIdx.x] = (int32_t)__builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4);
     out[2 * blockIdx.x + 1] = (int32_t)__builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate device memory
+// (pod_attn_plan_scratch): the plan's workspace -- counters, work lists and
+// split partials -- lives in this array.  Each device holds its own copy for
+// the life of the process.  In host code `scratch` names a host-side stand-in,
+// never the device memory: the device address is taken once per device with
+// hipGetSymbolAddress (that device current) and only that address is used.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+hipError_t scratch_address(int device, void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[device] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[device] = p;
+  }
+  *out = addr[device];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------
