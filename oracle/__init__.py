@@ -45,6 +45,7 @@ nothing.
 
 from .attention import (  # noqa: F401
     bf16_bits_to_f64,
+    fp8_e4m3_bits_to_f64,
     kv_head_of,
     visible_key_count,
     attention_rows,

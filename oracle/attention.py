@@ -31,6 +31,12 @@ Readings of the pages (they are silent on each point):
 * R4  LSE is the natural-log log-sum-exp of the *scaled* scores.
 * R5  a split restricted to keys [b, e) with no visible key has O = 0 and
       LSE = -inf and carries zero weight in the merge.
+* R6  an FP8 KV cache ("Prefill vs. Decode GPU Utilization Imbalance",
+      section on quantization as a lever on the bandwidth and capacity
+      problem, names quantized KV caches without fixing a format) holds OCP
+      FP8 E4M3 bytes with one float32 scale per KV head for K and one for V:
+      the key or value is the decoded byte times its head's scale, and the
+      attention is that of the decoded values.
 
 No online softmax, no tiling and no splitting is used in
 :func:`attention_rows`; each row's softmax sees the whole row at once (max,
@@ -65,6 +71,23 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
         raise TypeError("expected uint16 bfloat16 bit patterns")
     f32 = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
     return f32.astype(np.float64)
+
+
+def fp8_e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of OCP FP8 E4M3 bytes (uint8), from the format's
+    definition: sign bit, 4 exponent bits with bias 7, 3 mantissa bits; an
+    exponent field of 0 is subnormal (mantissa * 2^-6 / 8); S.1111.111 is NaN
+    and the format has no infinities (reading R6)."""
+    bits = np.asarray(bits)
+    if bits.dtype != np.uint8:
+        raise TypeError("expected uint8 E4M3 bytes")
+    b = bits.astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 0xF) & (m == 7), np.nan, mag)
+    return sign * mag
 
 
 # ---------------------------------------------------------------------------
@@ -211,7 +234,8 @@ def merge_partials(parts: Sequence[Tuple[np.ndarray, np.ndarray]]):
 def gather_request_kv(batch: Dict, r: int, kv_len: int,
                       tokens: Optional[np.ndarray] = None):
     """Keys and values (float64 [kv_len, Hkv, d]) of request ``r`` (prefill
-    requests first, then decodes) read from the batch's KV cache.
+    requests first, then decodes) read from the batch's KV cache (bfloat16,
+    or FP8 E4M3 bytes with per-KV-head scales, reading R6).
 
     Contiguous layout: rows kv_indptr[r] .. kv_indptr[r] + kv_len.
     Paged layout: the request's pages page_indices[page_indptr[r]:...] in
@@ -233,6 +257,12 @@ def gather_request_kv(batch: Dict, r: int, kv_len: int,
         sl = tokens % ps
         k = kc[pg, sl]
         v = vc[pg, sl]
+    if batch.get("kv_dtype", "bf16") == "fp8_e4m3":
+        # reading R6: decoded byte times the KV head's scale
+        ks = np.asarray(batch["k_scale"], dtype=np.float64)
+        vs = np.asarray(batch["v_scale"], dtype=np.float64)
+        return (fp8_e4m3_bits_to_f64(k) * ks[None, :, None],
+                fp8_e4m3_bits_to_f64(v) * vs[None, :, None])
     return bf16_bits_to_f64(k), bf16_bits_to_f64(v)
 
 

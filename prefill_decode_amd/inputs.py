@@ -24,6 +24,12 @@ Llama-3-8B-shaped layers).  No dataset is involved; every value is synthetic:
 Conventions: request order is all prefill requests, then all decodes;
 ``uniform in [a, b]`` is integers with both ends included; Q/K/V values are
 i.i.d. N(0, 1) drawn in float32 and rounded to bfloat16 (nearest-even).
+
+FP8 KV caches (``kv_dtype="fp8_e4m3"``, decode-only batches): K and V are
+drawn the same way in float32, each KV head gets the scale max|x| / 448 over
+its pool (float32), and the cache holds x / scale encoded as OCP FP8 E4M3
+(nearest, ties to even) -- so that the largest value of a head is the format's
+largest finite value.
 """
 
 from __future__ import annotations
@@ -37,6 +43,8 @@ import numpy as np
 HEAD_DIM = 128
 PAGE_SIZE = 16
 BF16_NAN = 0x7FC0
+FP8_NAN = 0x7F              # E4M3: S.1111.111 is the only NaN pattern
+FP8_MAX = 448.0
 
 # rng stream tags
 _TAG_LEN, _TAG_PAGES, _TAG_QP, _TAG_K, _TAG_V, _TAG_QD = 0, 1, 2, 3, 4, 5
@@ -59,6 +67,7 @@ class BatchSpec:
     head_dim: int = HEAD_DIM
     random_pages: bool = True
     extra_pages: int = 3             # unreferenced pool pages (poisoned)
+    kv_dtype: str = "bf16"           # "bf16" | "fp8_e4m3"
 
     @property
     def num_prefill(self) -> int:
@@ -138,6 +147,47 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
+def _fp8_e4m3_code_values() -> np.ndarray:
+    """Values of the non-negative finite E4M3 codes 0x00 .. 0x7E, in code
+    order (which is increasing order): exponent field 0 gives m * 2^-9,
+    otherwise (1 + m/8) * 2^(e - 7)."""
+    codes = np.arange(0x7F)
+    e, m = codes >> 3, codes & 7
+    return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+_FP8_VALUES = _fp8_e4m3_code_values()
+
+
+def f32_to_fp8_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Encode finite values with |x| <= 448 as E4M3 bytes, rounding to the
+    nearest code and, on a tie, to the code with an even mantissa."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(a > FP8_MAX) or not np.all(np.isfinite(x)):
+        raise ValueError("value outside the E4M3 range")
+    v = _FP8_VALUES
+    i = np.clip(np.searchsorted(v, a, side="left"), 1, len(v) - 1)   # v[i-1] < a <= v[i]
+    lo, hi = v[i - 1], v[i]
+    pick_hi = (a - lo > hi - a) | ((a - lo == hi - a) & (i % 2 == 0))
+    code = np.where(a <= v[0], 0, np.where(pick_hi, i, i - 1)).astype(np.uint8)
+    return (code | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)).astype(np.uint8)
+
+
+def _fp8_pool(seed: int, tag: int, shape, chunk: int):
+    """(E4M3 bytes, per-KV-head float32 scales) of an N(0, 1) float32 pool of
+    shape [..., Hkv, d] drawn as the bf16 pools are."""
+    lead = shape[0]
+    x = np.empty(shape, dtype=np.float32)
+    for c0 in range(0, lead, chunk):
+        c1 = min(lead, c0 + chunk)
+        rng = np.random.default_rng([seed, tag, c0 // chunk])
+        x[c0:c1] = rng.standard_normal((c1 - c0,) + tuple(shape[1:]), dtype=np.float32)
+    axes = tuple(range(x.ndim - 2)) + (x.ndim - 1,)
+    scale = (np.max(np.abs(x), axis=axes) / np.float32(FP8_MAX)).astype(np.float32)
+    return f32_to_fp8_e4m3_bits(x / scale[:, None]), scale
+
+
 def _normal_bf16(seed: int, tag: int, shape, chunk: Optional[int] = None) -> np.ndarray:
     if chunk is None:
         rng = np.random.default_rng([seed, tag])
@@ -179,6 +229,7 @@ def _base_dict(spec: BatchSpec) -> Dict:
         "page_size": spec.page_size,
         "causal": spec.causal,
         "sm_scale": spec.sm_scale,
+        "kv_dtype": spec.kv_dtype,
         "prefill_qo_len": np.array(spec.prefill_qo_len, dtype=np.int32),
         "prefill_kv_len": np.array(spec.prefill_kv_len, dtype=np.int32),
         "decode_kv_len": np.array(spec.decode_kv_len, dtype=np.int32),
@@ -191,41 +242,51 @@ def make_batch_host(spec: BatchSpec, poison: bool = True) -> Dict:
     Keys: q_prefill [sum qo, Hq, d], q_decode [n_dec, Hq, d], k_cache and
     v_cache ([pool, page_size, Hkv, d] paged, or [sum kv, Hkv, d]
     contiguous), page_indptr/page_indices (paged) or kv_indptr
-    (contiguous), plus the spec's scalars and lengths.  With ``poison``,
-    KV slots that belong to no token (tails of last pages, unreferenced
-    pages) hold bf16 NaN so that a reader of them is caught.
+    (contiguous), plus the spec's scalars and lengths.  An FP8 batch holds
+    E4M3 bytes (uint8) in k_cache / v_cache and float32 k_scale / v_scale
+    [Hkv].  With ``poison``, KV slots that belong to no token (tails of last
+    pages, unreferenced pages) hold NaN so that a reader of them is caught.
     """
     b = _base_dict(spec)
     hq, hkv, d = spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
     sum_qo = int(sum(spec.prefill_qo_len))
+    fp8 = spec.kv_dtype == "fp8_e4m3"
+    nan = FP8_NAN if fp8 else BF16_NAN
     b["q_prefill"] = _normal_bf16(spec.seed, _TAG_QP, (sum_qo, hq, d))
     b["q_decode"] = _normal_bf16(spec.seed, _TAG_QD, (spec.num_decode, hq, d))
+
+    def pools(shape, chunk):
+        if fp8:
+            b["k_cache"], b["k_scale"] = _fp8_pool(spec.seed, _TAG_K, shape, chunk)
+            b["v_cache"], b["v_scale"] = _fp8_pool(spec.seed, _TAG_V, shape, chunk)
+        else:
+            b["k_cache"] = _normal_bf16(spec.seed, _TAG_K, shape, chunk=chunk)
+            b["v_cache"] = _normal_bf16(spec.seed, _TAG_V, shape, chunk=chunk)
+
     if spec.layout == "contiguous":
         lens = np.array(spec.kv_lens, dtype=np.int64)
         indptr = np.zeros(len(lens) + 1, dtype=np.int32)
         indptr[1:] = np.cumsum(lens)
         n = int(indptr[-1])
         b["kv_indptr"] = indptr
-        b["k_cache"] = _normal_bf16(spec.seed, _TAG_K, (n, hkv, d), chunk=65536)
-        b["v_cache"] = _normal_bf16(spec.seed, _TAG_V, (n, hkv, d), chunk=65536)
+        pools((n, hkv, d), 65536)
         return b
     indptr, indices, pool = page_table(spec)
     ps = spec.page_size
     b["page_indptr"] = indptr
     b["page_indices"] = indices
-    b["k_cache"] = _normal_bf16(spec.seed, _TAG_K, (pool, ps, hkv, d), chunk=_CHUNK_PAGES)
-    b["v_cache"] = _normal_bf16(spec.seed, _TAG_V, (pool, ps, hkv, d), chunk=_CHUNK_PAGES)
+    pools((pool, ps, hkv, d), _CHUNK_PAGES)
     if poison:
         used = np.zeros(pool, dtype=bool)
         used[indices] = True
-        b["k_cache"][~used] = BF16_NAN
-        b["v_cache"][~used] = BF16_NAN
+        b["k_cache"][~used] = nan
+        b["v_cache"][~used] = nan
         for r, L in enumerate(spec.kv_lens):
             tail = L % ps
             if tail:
                 last = indices[indptr[r + 1] - 1]
-                b["k_cache"][last, tail:] = BF16_NAN
-                b["v_cache"][last, tail:] = BF16_NAN
+                b["k_cache"][last, tail:] = nan
+                b["v_cache"][last, tail:] = nan
     return b
 
 
@@ -257,25 +318,49 @@ def make_batch_device(spec: BatchSpec, device="cuda", poison: bool = False) -> D
                                      dtype=torch.float32, device=device).to(torch.bfloat16)
         return out
 
+    def fp8_pool(tag, shape, chunk_rows):
+        # float32 draws as for bf16, per-KV-head scale max|x| / 448, then
+        # torch's E4M3 conversion (nearest, ties to even) of x / scale
+        x = torch.empty(shape, dtype=torch.float32, device=device)
+        for c0 in range(0, shape[0], chunk_rows):
+            c1 = min(shape[0], c0 + chunk_rows)
+            gen.manual_seed(int(spec.seed) * 1000003 + tag * 7919 + c0 // chunk_rows)
+            x[c0:c1] = torch.randn((c1 - c0,) + tuple(shape[1:]), generator=gen,
+                                   dtype=torch.float32, device=device)
+        dims = tuple(range(x.dim() - 2)) + (x.dim() - 1,)
+        scale = (x.abs().amax(dim=dims) / FP8_MAX).float()
+        q = (x / scale[:, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        del x
+        return q, scale
+
     sum_qo = int(sum(spec.prefill_qo_len))
+    fp8 = spec.kv_dtype == "fp8_e4m3"
     b["q_prefill"] = normal(_TAG_QP, (sum_qo, hq, d))
     b["q_decode"] = normal(_TAG_QD, (spec.num_decode, hq, d))
+
+    def pools(shape, chunk_rows):
+        if fp8:
+            b["k_cache"], b["k_scale"] = fp8_pool(_TAG_K, shape, chunk_rows)
+            b["v_cache"], b["v_scale"] = fp8_pool(_TAG_V, shape, chunk_rows)
+        else:
+            b["k_cache"] = normal(_TAG_K, shape, chunk_rows)
+            b["v_cache"] = normal(_TAG_V, shape, chunk_rows)
+
     if spec.layout == "contiguous":
         lens = np.array(spec.kv_lens, dtype=np.int64)
         indptr = np.zeros(len(lens) + 1, dtype=np.int32)
         indptr[1:] = np.cumsum(lens)
         b["kv_indptr"] = indptr
         n = int(indptr[-1])
-        b["k_cache"] = normal(_TAG_K, (n, hkv, d), 1 << 18)
-        b["v_cache"] = normal(_TAG_V, (n, hkv, d), 1 << 18)
+        pools((n, hkv, d), 1 << 18)
         return b
     indptr, indices, pool = page_table(spec)
     b["page_indptr"] = indptr
     b["page_indices"] = indices
-    b["k_cache"] = normal(_TAG_K, (pool, spec.page_size, hkv, d), 16384)
-    b["v_cache"] = normal(_TAG_V, (pool, spec.page_size, hkv, d), 16384)
+    pools((pool, spec.page_size, hkv, d), 16384)
     if poison:
-        nan = torch.tensor(float("nan"), dtype=torch.bfloat16, device=device)
+        nan = torch.tensor(FP8_NAN, dtype=torch.uint8, device=device) if fp8 else \
+            torch.tensor(float("nan"), dtype=torch.bfloat16, device=device)
         used = np.zeros(pool, dtype=bool)
         used[indices] = True
         unused = torch.from_numpy(np.nonzero(~used)[0]).to(device)
@@ -301,6 +386,11 @@ def host_subset(batch_dev: Dict, prefill_ids: Sequence[int],
     spec_keys = ["name", "num_qo_heads", "num_kv_heads", "head_dim", "layout",
                  "page_size", "causal", "sm_scale"]
     out = {k: batch_dev[k] for k in spec_keys}
+    out["kv_dtype"] = batch_dev.get("kv_dtype", "bf16")
+    for key in ("k_scale", "v_scale"):
+        if key in batch_dev:
+            v = batch_dev[key]
+            out[key] = v.cpu().numpy() if hasattr(v, "cpu") else np.asarray(v)
     pqo = np.asarray(batch_dev["prefill_qo_len"])
     pkv = np.asarray(batch_dev["prefill_kv_len"])
     dkv = np.asarray(batch_dev["decode_kv_len"])
@@ -313,6 +403,8 @@ def host_subset(batch_dev: Dict, prefill_ids: Sequence[int],
     out["decode_kv_len"] = dkv[decode_ids].astype(np.int32)
 
     def bits(t):
+        if t.dtype == torch.uint8:
+            return t.contiguous().cpu().numpy()
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
     qp = [bits(batch_dev["q_prefill"][int(offs[r]):int(offs[r + 1])]) for r in prefill_ids]
@@ -355,6 +447,12 @@ def to_device(batch: Dict, device="cuda") -> Dict:
 
     out = dict(batch)
     for key in ("q_prefill", "q_decode", "k_cache", "v_cache"):
-        a = np.ascontiguousarray(batch[key]).view(np.int16)
-        out[key] = torch.from_numpy(a).to(device).view(torch.bfloat16)
+        a = np.ascontiguousarray(batch[key])
+        if a.dtype == np.uint8:
+            out[key] = torch.from_numpy(a).to(device)
+        else:
+            out[key] = torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    for key in ("k_scale", "v_scale"):
+        if key in batch:
+            out[key] = torch.from_numpy(np.ascontiguousarray(batch[key], np.float32)).to(device)
     return out

@@ -24,6 +24,11 @@ What each pin rests on:
                   row, decodes in shuffled order)
   sample_rows_match_batch the row-sampling entry point against the whole-batch
                   oracle on a paged batch of several chunks and decodes
+  fp8_codes       E4M3 bytes: values the format's table fixes, and torch's own
+                  float8_e4m3fn decoding of all 256 codes
+  fp8_batch_is_dequantized_bf16  an FP8 batch with power-of-two per-head
+                  scales equals the bf16 batch holding the decoded values
+                  (exact in bf16), different scales per head and for K and V
 """
 
 import math
@@ -367,7 +372,50 @@ def pin_sample_rows_match_batch():
         assert np.max(np.abs(out[key] - full[key][idx])) <= 1e-13, key
 
 
+def pin_fp8_codes():
+    table = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x3C: 1.5, 0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0x80: -0.0, 0xB8: -1.0,
+             0xFE: -448.0}
+    got = oa.fp8_e4m3_bits_to_f64(np.array(list(table), dtype=np.uint8))
+    for g_, w in zip(got, table.values()):
+        assert g_ == w and np.signbit(g_) == np.signbit(w), (g_, w)
+    nan = oa.fp8_e4m3_bits_to_f64(np.array([0x7F, 0xFF], dtype=np.uint8))
+    assert np.all(np.isnan(nan))
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    mine = oa.fp8_e4m3_bits_to_f64(codes)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.all(np.diff(mine[:0x7F]) > 0)                   # codes 0..0x7E increase
+
+
+def pin_fp8_batch_is_dequantized_bf16():
+    spec = inputs.custom_spec("f8", 4, 2, [], [5, 13, 1], seed=34, head_dim=8, page_size=4,
+                              extra_pages=1, kv_dtype="fp8_e4m3")
+    b8 = inputs.make_batch_host(spec, poison=False)
+    b8["k_scale"] = np.array([2.0 ** -3, 2.0 ** -1], dtype=np.float32)
+    b8["v_scale"] = np.array([2.0 ** -2, 2.0], dtype=np.float32)
+    out8 = oracle.batch_attention(b8, workers=1)
+    # the same batch in bf16: the decoded values, exact in bf16 (3 mantissa
+    # bits times a power of two), computed without the oracle's decoder
+    import torch
+    bb = dict(b8)
+    bb["kv_dtype"] = "bf16"
+    for key, sc in (("k_cache", "k_scale"), ("v_cache", "v_scale")):
+        x = torch.from_numpy(b8[key]).view(torch.float8_e4m3fn).float().numpy()
+        x = x * b8[sc][None, None, :, None]
+        bb[key] = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal(bb[key].astype(np.uint32) << 16, x.astype(np.float32).view(np.uint32))
+    outb = oracle.batch_attention(bb, workers=1)
+    for k in ("o_decode", "lse_decode"):
+        assert np.all(np.isfinite(out8[k])), k
+        assert np.max(np.abs(out8[k] - outb[k])) <= 1e-13, k
+
+
 ALL_PINS = [pin_bruteforce, pin_rows_sum_to_one, pin_single_key,
             pin_decode_is_last_prefill_row, pin_split_merge, pin_identical_keys,
             pin_boundary_probe, pin_gqa_is_mha, pin_sdpa, pin_page_invariance,
-            pin_bf16_upcast, pin_sample_rows_bruteforce, pin_sample_rows_match_batch]
+            pin_bf16_upcast, pin_sample_rows_bruteforce, pin_sample_rows_match_batch,
+            pin_fp8_codes, pin_fp8_batch_is_dequantized_bf16]

@@ -14,6 +14,29 @@ from tests import oracle_pins
 
 _real_gather = oa.gather_request_kv
 _real_merge = oa.merge_partials
+_real_fp8 = oa.fp8_e4m3_bits_to_f64
+
+
+def _fp8_bias8(bits):
+    # the exponent bias of the other FP8 convention (8 instead of 7)
+    return _real_fp8(bits) * 0.5
+
+
+def _gather_v_scale_on_k(batch, r, kv_len, tokens=None):
+    k, v = _real_gather(batch, r, kv_len, tokens)
+    if batch.get("kv_dtype") == "fp8_e4m3":
+        ks = np.asarray(batch["k_scale"], np.float64)
+        vs = np.asarray(batch["v_scale"], np.float64)
+        k = k / ks[None, :, None] * vs[None, :, None]
+    return k, v
+
+
+def _gather_scales_other_head(batch, r, kv_len, tokens=None):
+    k, v = _real_gather(batch, r, kv_len, tokens)
+    if batch.get("kv_dtype") == "fp8_e4m3":
+        ks = np.asarray(batch["k_scale"], np.float64)
+        k = k / ks[None, :, None] * ks[::-1][None, :, None]
+    return k, v
 
 
 def _swap_kv(batch, r, kv_len, tokens=None):
@@ -52,6 +75,9 @@ MUTANTS = {
                          .view(np.float32).astype(np.float64)),
     "kv_swapped": ("gather_request_kv", _swap_kv),
     "merge_unnormalised": ("merge_partials", _merge_no_norm),
+    "fp8_bias8": ("fp8_e4m3_bits_to_f64", _fp8_bias8),
+    "fp8_v_scale_on_k": ("gather_request_kv", _gather_v_scale_on_k),
+    "fp8_scales_other_head": ("gather_request_kv", _gather_scales_other_head),
     # a chunk's first row handed to the request before it
     "sample_row_to_previous_request": (
         "_request_of_row", lambda offs, g: int(np.searchsorted(offs, g, side="left") - 1)),
