@@ -62,6 +62,14 @@ typedef enum {
 
 typedef enum { POD_KV_CONTIGUOUS = 0, POD_KV_PAGED = 1 } pod_kv_layout_t;
 
+/* Element type of the KV cache.  POD_KV_FP8_E4M3: OCP FP8 E4M3 bytes with
+ * one fp32 scale per KV head for K and one for V (value = decoded byte times
+ * its head's scale); a lever on decode's bytes named in "Prefill vs. Decode
+ * GPU Utilization Imbalance", section "Quantization and compression as a
+ * lever on both the bandwidth and capacity problem".  Supported for
+ * decode-only batches with a contiguous cache or pages of >= 16 tokens. */
+typedef enum { POD_KV_BF16 = 0, POD_KV_FP8_E4M3 = 1 } pod_kv_dtype_t;
+
 /* Scheduler modes of the fused kernel: how the two workgroups of each CU
  * pick their first role (every workgroup moves to the other queue when its
  * own runs dry, so all modes run every unit exactly once). */
@@ -100,6 +108,7 @@ typedef struct {
   int32_t page_size;      /* PAGED: power of two in [1, 1024]; ignored otherwise */
   int32_t causal;         /* 1: bottom-right causal chunks; 0: full visibility */
   float sm_scale;         /* finite, > 0; multiplies the fp32 score */
+  int32_t kv_dtype;       /* pod_kv_dtype_t */
 } pod_attn_params_t;
 
 typedef struct {
@@ -162,7 +171,8 @@ typedef struct {
 /* Tensors of one run.  bf16 = IEEE bfloat16.  Row-major, no padding:
  *   q_prefill  device bf16 [sum(prefill qo_len), Hq, 128]  (requests in order)
  *   q_decode   device bf16 [num_decode, Hq, 128]
- *   k, v       device bf16 CONTIGUOUS: [sum(kv_len), Hkv, 128] with request r's
+ *   k, v       device bf16 (or E4M3 bytes, kv_dtype FP8) CONTIGUOUS:
+ *                          [sum(kv_len), Hkv, 128] with request r's
  *                          tokens at rows kv_indptr[r] ..;
  *                          PAGED: [num_pages, page_size, Hkv, 128]; token t of
  *                          request r is slot t % page_size of page
@@ -172,6 +182,7 @@ typedef struct {
  *   page_indices device int32 [page_indptr[last]]             (PAGED)
  *   o_prefill, o_decode     device bf16, shapes of q_prefill / q_decode
  *   lse_prefill, lse_decode device fp32 [rows, Hq], natural log; may be NULL
+ *   k_scale, v_scale        device fp32 [Hkv] (kv_dtype FP8 only; else unused)
  * Request order everywhere: the prefill requests, then the decodes.  Slots of
  * pages past a request's kv_len are never read.  Base pointers must be 16-byte
  * aligned.  Unlike common paged-attention interfaces there is no per-request
@@ -190,6 +201,8 @@ typedef struct {
   void* o_decode;
   float* lse_prefill;
   float* lse_decode;
+  const float* k_scale;
+  const float* v_scale;
 } pod_attn_tensors_t;
 
 /* Plans one hybrid batch for the current HIP device: validates the lengths,
@@ -209,9 +222,13 @@ typedef struct {
  * `stream`, and returns a plan that refers to `workspace` (which must then
  * stay alive and unshared until pod_attn_plan_destroy).  Runs of one plan on
  * different streams must not overlap: they share the workspace.
- * Errors: POD_ERR_INVALID_ARGUMENT (lengths, heads, scale, layout, NULL
- * length arrays with a nonzero count), POD_ERR_UNSUPPORTED (head_dim != 128,
- * wgs_per_cu other than 0 or 2), POD_ERR_WORKSPACE_TOO_SMALL, POD_ERR_HIP. */
+ * Errors: POD_ERR_INVALID_ARGUMENT (lengths, heads, scale, layout, dtype,
+ * NULL length arrays with a nonzero count), POD_ERR_UNSUPPORTED (head_dim !=
+ * 128, wgs_per_cu other than 0 or 2, an FP8 cache with prefill requests or
+ * pages of fewer than 16 tokens), POD_ERR_WORKSPACE_TOO_SMALL, POD_ERR_HIP.
+ * With an FP8 cache (decode-only) every run entry point runs the FP8 decode
+ * kernel and the merge (there is no prefill to fuse with); the
+ * batched-prefill comparator is not available. */
 pod_status_t pod_attn_plan(const pod_attn_params_t* params,
                            int32_t num_prefill, const int32_t* prefill_qo_len,
                            const int32_t* prefill_kv_len,

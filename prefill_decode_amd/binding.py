@@ -24,6 +24,7 @@ POD_OK = 0
 STATUS = {0: "POD_OK", 1: "POD_ERR_INVALID_ARGUMENT", 2: "POD_ERR_UNSUPPORTED",
           3: "POD_ERR_WORKSPACE_TOO_SMALL", 4: "POD_ERR_HIP", 5: "POD_ERR_INTERNAL"}
 KV_CONTIGUOUS, KV_PAGED = 0, 1
+KV_BF16, KV_FP8_E4M3 = 0, 1
 SCHED_AUTO, SCHED_COLOCATE, SCHED_ORDERED, SCHED_SPLIT = 0, 1, 2, 3
 FLAG_TRACE = 0x1
 FLAG_BATCHED_PREFILL = 0x2
@@ -46,7 +47,7 @@ class PodError(RuntimeError):
 class Params(C.Structure):
     _fields_ = [("num_qo_heads", C.c_int32), ("num_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("kv_layout", C.c_int32), ("page_size", C.c_int32),
-                ("causal", C.c_int32), ("sm_scale", C.c_float)]
+                ("causal", C.c_int32), ("sm_scale", C.c_float), ("kv_dtype", C.c_int32)]
 
 
 class Tuning(C.Structure):
@@ -79,7 +80,7 @@ class Tensors(C.Structure):
                 ("v", C.c_void_p), ("kv_indptr", C.c_void_p), ("page_indptr", C.c_void_p),
                 ("page_indices", C.c_void_p), ("o_prefill", C.c_void_p),
                 ("o_decode", C.c_void_p), ("lse_prefill", C.c_void_p),
-                ("lse_decode", C.c_void_p)]
+                ("lse_decode", C.c_void_p), ("k_scale", C.c_void_p), ("v_scale", C.c_void_p)]
 
 
 def lib():
@@ -150,12 +151,13 @@ def _ptr(a: np.ndarray):
 
 
 def make_params(num_qo_heads, num_kv_heads, layout="paged", page_size=16, causal=True,
-                sm_scale=None, head_dim=128) -> Params:
+                sm_scale=None, head_dim=128, kv_dtype="bf16") -> Params:
     if sm_scale is None:
         sm_scale = 1.0 / np.sqrt(head_dim)
     lay = KV_PAGED if layout in ("paged", KV_PAGED) else KV_CONTIGUOUS
+    dt = KV_FP8_E4M3 if kv_dtype in ("fp8_e4m3", KV_FP8_E4M3) else KV_BF16
     return Params(int(num_qo_heads), int(num_kv_heads), int(head_dim), lay, int(page_size),
-                  1 if causal else 0, float(sm_scale))
+                  1 if causal else 0, float(sm_scale), dt)
 
 
 def make_tuning(wgs_per_cu=0, prefill_quarters_per_cu=-1, prefill_kv_splits=0,
@@ -270,10 +272,10 @@ def _dp(t):
 
 def make_tensors(q_prefill=None, q_decode=None, k=None, v=None, kv_indptr=None,
                  page_indptr=None, page_indices=None, o_prefill=None, o_decode=None,
-                 lse_prefill=None, lse_decode=None) -> Tensors:
+                 lse_prefill=None, lse_decode=None, k_scale=None, v_scale=None) -> Tensors:
     return Tensors(_dp(q_prefill), _dp(q_decode), _dp(k), _dp(v), _dp(kv_indptr),
                    _dp(page_indptr), _dp(page_indices), _dp(o_prefill), _dp(o_decode),
-                   _dp(lse_prefill), _dp(lse_decode))
+                   _dp(lse_prefill), _dp(lse_decode), _dp(k_scale), _dp(v_scale))
 
 
 def run(p: Plan, tensors: Tensors, stream=None):
@@ -348,7 +350,8 @@ class BatchRunner:
         self.batch = batch
         b = batch
         self.params = make_params(b["num_qo_heads"], b["num_kv_heads"], b["layout"],
-                                  b["page_size"], b["causal"], b["sm_scale"], b["head_dim"])
+                                  b["page_size"], b["causal"], b["sm_scale"], b["head_dim"],
+                                  b.get("kv_dtype", "bf16"))
 
         def dev(x, dtype=None):
             if isinstance(x, torch.Tensor):
@@ -356,6 +359,8 @@ class BatchRunner:
             if isinstance(x, np.ndarray) and x.dtype == np.uint16:
                 return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device) \
                     .view(torch.bfloat16)
+            if isinstance(x, np.ndarray) and x.dtype in (np.uint8, np.float32):
+                return torch.from_numpy(np.ascontiguousarray(x)).to(device)
             return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.int32))) \
                 .to(device)
 
@@ -366,6 +371,8 @@ class BatchRunner:
         self.kv_indptr = dev(b["kv_indptr"]) if "kv_indptr" in b else None
         self.page_indptr = dev(b["page_indptr"]) if "page_indptr" in b else None
         self.page_indices = dev(b["page_indices"]) if "page_indices" in b else None
+        self.k_scale = dev(b["k_scale"]) if "k_scale" in b else None
+        self.v_scale = dev(b["v_scale"]) if "v_scale" in b else None
         hq = b["num_qo_heads"]
         self.o_prefill = torch.empty_like(self.q_prefill)
         self.o_decode = torch.empty_like(self.q_decode)
@@ -378,7 +385,7 @@ class BatchRunner:
         self.tensors = make_tensors(self.q_prefill, self.q_decode, self.k, self.v,
                                     self.kv_indptr, self.page_indptr, self.page_indices,
                                     self.o_prefill, self.o_decode, self.lse_prefill,
-                                    self.lse_decode)
+                                    self.lse_decode, self.k_scale, self.v_scale)
 
     def run(self, stream=None):
         run(self.plan, self.tensors, stream)

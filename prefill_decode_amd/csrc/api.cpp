@@ -205,8 +205,12 @@ pod_status_t check_tensors(const pod_attn_plan_s* pl, const pod_attn_tensors_t* 
     if ((st = need(t->q_decode, "q_decode")) != POD_OK) return st;
     if ((st = need(t->o_decode, "o_decode")) != POD_OK) return st;
   }
+  if (pl->batch.params.kv_dtype == POD_KV_FP8_E4M3 && has_d && (!t->k_scale || !t->v_scale))
+    return set_err(POD_ERR_INVALID_ARGUMENT, "k_scale/v_scale is NULL (FP8 KV cache)");
   return POD_OK;
 }
+
+bool is_fp8(const pod_attn_plan_s* pl) { return pl->batch.params.kv_dtype == POD_KV_FP8_E4M3; }
 
 int kv_mode_of(const pod_attn_plan_s* pl) {
   const auto& p = pl->batch.params;
@@ -248,6 +252,8 @@ KernelArgs make_args(const pod_attn_plan_s* pl, const pod_attn_tensors_t* t, con
   a.o_decode = (uint16_t*)t->o_decode;
   a.lse_prefill = t->lse_prefill;
   a.lse_decode = t->lse_decode;
+  a.k_scale = t->k_scale;
+  a.v_scale = t->v_scale;
   a.part_o = (float*)(pl->ws + pl->off_part_o);
   a.part_lse = (float*)(pl->ws + pl->off_part_lse);
   a.p_items = (const int32_t*)(pl->ws + dl.p_items);
@@ -428,7 +434,12 @@ pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t
   hipError_t e;
   if (before_fused && (e = hipEventRecord(before_fused, stream)) != hipSuccess)
     return hip_err(e, "hipEventRecord(before_fused)");
-  if (grid > 0) {
+  if (is_fp8(pl)) {
+    // decode-only FP8 batch: nothing to fuse with; the FP8 decode kernel
+    if (w.n_groups() > 0 && (e = launch_decode_fp8(a, kv_mode_of(pl), w.n_groups(), stream)) !=
+                                hipSuccess)
+      return hip_err(e, "FP8 decode kernel launch");
+  } else if (grid > 0) {
     e = launch_fused(a, kv_mode_of(pl), grid, stream);
     if (e != hipSuccess) return hip_err(e, "fused kernel launch");
     if (!a.self_reset) ++pl->launches[kKindFused];
@@ -460,7 +471,8 @@ pod_status_t pod_attn_sequential_run(pod_attn_plan_t pl, const pod_attn_tensors_
     if (!a.self_reset) ++pl->launches[kKindSeq];
   }
   if (w.n_groups() > 0) {
-    hipError_t e = launch_decode(a, kvm, w.n_groups(), stream);
+    hipError_t e = is_fp8(pl) ? launch_decode_fp8(a, kvm, w.n_groups(), stream)
+                              : launch_decode(a, kvm, w.n_groups(), stream);
     if (e != hipSuccess) return hip_err(e, "decode kernel launch");
   }
   return launch_merge_of(a, w, stream);
@@ -489,7 +501,9 @@ pod_status_t pod_attn_streams_run(pod_attn_plan_t pl, const pod_attn_tensors_t* 
       return hip_err(e, "prefill kernel launch");
     if (!a.self_reset) ++pl->launches[kKindSeq];
   }
-  if (w.n_groups() > 0 && (e = launch_decode(a, kvm, w.n_groups(), decode_stream)) != hipSuccess)
+  if (w.n_groups() > 0 &&
+      (e = is_fp8(pl) ? launch_decode_fp8(a, kvm, w.n_groups(), decode_stream)
+                      : launch_decode(a, kvm, w.n_groups(), decode_stream)) != hipSuccess)
     return hip_err(e, "decode kernel launch");
   // join: the merge (and whatever the caller enqueues next) waits for both
   if ((e = hipEventRecord(pl->ev_join, decode_stream)) != hipSuccess)

@@ -78,12 +78,15 @@ struct KernelArgs {
   // .. + merge_splits - 1 into row t of o_prefill / lse_prefill
   int32_t merge_splits;
   float merge_lse_scale;  // factor taking part_lse to log2 (1, or log2(e) for natural log)
+  const float* k_scale;   // FP8 KV: per-KV-head scales (device fp32 [Hkv])
+  const float* v_scale;
 };
 
 hipError_t launch_fused(const KernelArgs& a, int kv_mode, int grid, hipStream_t s);
 hipError_t launch_prefill(const KernelArgs& a, int kv_mode, int grid, hipStream_t s,
                           bool batched = false);
 hipError_t launch_decode(const KernelArgs& a, int kv_mode, int grid, hipStream_t s);
+hipError_t launch_decode_fp8(const KernelArgs& a, int kv_mode, int grid, hipStream_t s);
 hipError_t launch_merge(const KernelArgs& a, int grid, hipStream_t s);
 hipError_t launch_probe(int32_t* out, int blocks, hipStream_t s);
 

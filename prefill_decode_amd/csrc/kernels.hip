@@ -834,6 +834,232 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
 }
 
 // ---------------------------------------------------------------------------
+// Decode over an FP8 E4M3 KV cache with one scale per KV head for K and for
+// V ("Prefill vs. Decode GPU Utilization Imbalance", section "Quantization
+// and compression as a lever on both the bandwidth and capacity problem"):
+// half the bytes per key, the same unit and step structure as decode_unit.
+// A token's row of one head is one 128-byte line.
+//   K: whole lines into registers -- a 16-key block is two raw loads (x = 0,
+//      1; lane L: key 8x + (L & 7), 16-byte chunk (L >> 3) ^ x) -- rebuilt
+//      by kop() into 16 keys x one chunk (chunk 2r + p for the 16-lane row r)
+//      and converted exactly to bf16: each chunk feeds two 16x16x32 MFMAs
+//      over d = 16 (2r + p) + 8 half + e (Q is loaded in that order).  The K
+//      scale multiplies the fp32 score together with sm_scale.
+//   V: the same whole-line loads into registers, converted to bf16 and
+//      written to the wave's LDS slice in decode_unit's layout (row = key,
+//      swizzled 16-byte chunks), then read transposed as there; the V scale
+//      multiplies the final O.
+// A step's raw K and V of the next step are in flight while it computes.
+// ---------------------------------------------------------------------------
+// eight E4M3 bytes (two dwords, byte order = element order) to eight bf16
+// (exact: E4M3 values are bf16 values)
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+#define POD_CVT(w, upper) \
+  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, upper))
+  return u32x4{POD_CVT(lo, false), POD_CVT(lo, true), POD_CVT(hi, false), POD_CVT(hi, true)};
+#undef POD_CVT
+}
+
+template <int KVM>
+__device__ __forceinline__ void decode_unit_fp8(const KernelArgs& a, cptr it, char* __restrict__ vbuf) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, q4 = lane >> 4;
+  const int qi = it[D_QROW], h0 = it[D_HEAD0], nq = it[D_NQ];
+  const int kb = it[D_KV_BEGIN], ke = it[D_KV_END], kvreq = it[D_KVREQ];
+  const int part = it[D_PART], pstride = it[D_PSTRIDE];
+  const int kvh = h0 / a.group;
+  constexpr uint32_t kRow8 = kHeadDim;               // bytes of one head's row
+  const uint32_t tok = (uint32_t)a.hkv * kRow8;
+  const char* kbase = (const char*)a.k + kvh * kRow8;
+  const char* vbase = (const char*)a.v + kvh * kRow8;
+  KvAddr<KVM> addr;
+  addr.init(a, kvreq);
+  const int span = ke - kb;
+  const int nsteps = (span + kDecodeStep - 1) / kDecodeStep;
+  const int nfull = span / kDecodeStep;
+  // the scales (uniform per unit) through the scalar cache
+  const float sl2 = a.scale_log2 * __builtin_bit_cast(float, ((cptr)a.k_scale)[kvh]);
+  const float vsc = __builtin_bit_cast(float, ((cptr)a.v_scale)[kvh]);
+
+  // Q operand kk = 2p + half: lane (query j, row q4) holds d = 32 q4 + 16 p + 8 half + e
+  u32x4 qf[4];
+  {
+    const bool ok = j < nq;
+    const uint16_t* qp = a.q_decode + ((int64_t)qi * a.hq + h0 + (ok ? j : 0)) * kHeadDim + 32 * q4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qf[kk] = ok ? *(const u32x4*)(qp + 8 * kk) : u32x4{0, 0, 0, 0};
+  }
+
+  const int lastb = (ke - 1) & ~15;
+  const int k8 = lane & 7, kc = lane >> 3;
+  struct Blk { __amdgpu_buffer_rsrc_t rk, rv; int rmax; };
+  auto block = [&](int s, int sb) {
+    const int bs = min(kb + s * kDecodeStep + 16 * sb, lastb);
+    const int64_t rw = addr.block_row(bs);
+    return Blk{rsrc(kbase + rw * tok), rsrc(vbase + rw * tok), ke - 1 - bs};
+  };
+  // raw loads of step s: k[2 sb + x] (chunk (L >> 3) ^ x), v[2 sb + x] (chunk L >> 3)
+  auto load = [&](int s, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const Blk bl = block(s, sb);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const uint32_t row = (uint32_t)min(8 * x + k8, bl.rmax) * tok;
+        kr[2 * sb + x] = bload<kStream>(bl.rk, row + 16u * (kc ^ x), 0);
+        vr[2 * sb + x] = bload<kStream>(bl.rv, row + 16u * kc, 0);
+      }
+    }
+  };
+  auto kop = [](const u32x4& A, const u32x4& B, int p) {
+    u32x4 r;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (p == 0) {
+        r[c] = (uint32_t)__builtin_amdgcn_update_dpp((int)A[c], (int)B[c], 0xE4, 0xF, 0xC, false);
+      } else {
+        const int t = __builtin_amdgcn_update_dpp(0, (int)A[c], 0x108, 0xF, 0x3, false);
+        r[c] = (uint32_t)__builtin_amdgcn_update_dpp(t, (int)B[c], 0x118, 0xF, 0xC, false);
+      }
+    }
+    return r;
+  };
+
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = kNegInf, l_run = 0.0f;
+  const int vrow0 = 4 * q4 + (j >> 2);
+  const int vsw = vswz(vrow0);
+
+  auto step = [&](int s, const u32x4 (&kr)[4], const u32x4 (&vr)[4], bool more) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) wait_vmem<8>();
+    else wait_vmem<0>();
+    // V(s): bf16 into the LDS slice (the previous step's transposed reads of
+    // it were issued earlier; one wave's LDS operations stay in order)
+    lds_fence();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * (i >> 1) + 8 * (i & 1) + k8;          // key row of the step
+      const u32x4 lo = fp8x8_to_bf16(vr[i][0], vr[i][1]);
+      const u32x4 hi = fp8x8_to_bf16(vr[i][2], vr[i][3]);
+      *(u32x4*)(vbuf + r * kRowBytes + 16 * ((2 * kc) ^ vswz(r))) = lo;
+      *(u32x4*)(vbuf + r * kRowBytes + 16 * ((2 * kc + 1) ^ vswz(r))) = hi;
+    }
+    lds_fence();
+    const int k0 = kb + s * kDecodeStep;
+    f32x4 s0 = {}, s1 = {};
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const u32x4 c0 = kop(kr[0], kr[1], p);
+      const u32x4 c1 = kop(kr[2], kr[3], p);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(fp8x8_to_bf16(c0[2 * hf], c0[2 * hf + 1])),
+                                                     as_bf(qf[2 * p + hf]), s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(fp8x8_to_bf16(c1[2 * hf], c1[2 * hf + 1])),
+                                                     as_bf(qf[2 * p + hf]), s1, 0, 0, 0);
+      }
+    }
+    float x[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = s0[r];
+      x[4 + r] = s1[r];
+    }
+    if (s >= nfull) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (k0 + 4 * q4 + r >= ke) x[r] = kNegInf;
+        if (k0 + 16 + 4 * q4 + r >= ke) x[4 + r] = kNegInf;
+      }
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) mx = fmax_(mx, x[r]);
+    mx = max_x32(max_x16(mx));
+    const float m_new = fmax_(m_run, mx * sl2);
+    if (any_lane(m_new > m_run)) {
+      const float alpha = exp2_(m_run - (m_new == kNegInf ? 0.0f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float nm = m_run == kNegInf ? 0.0f : -m_run;
+    float ls = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      x[r] = exp2_(__builtin_fmaf(x[r], sl2, nm));
+      ls += x[r];
+    }
+    l_run += ls;
+    const u32x4 pb = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                      pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+    const char* vt = vbuf + vrow0 * kRowBytes + 8 * (j & 1);
+    u32x4 af[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const char* cp = vt + 16 * ((2 * db + ((j & 3) >> 1)) ^ vsw);
+      const u32x2 lo = tr_read(cp);
+      const u32x2 hi = tr_read(cp + 16 * kRowBytes);
+      af[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+    lds_fence();
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(af[db]), as_bf(pb), o[db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  u32x4 ka[4], va[4], kn[4], vn[4];
+  if (nsteps > 0) {
+    load(0, ka, va);
+    int s = 0;
+    for (; s + 2 < nsteps; s += 2) {
+      load(s + 1, kn, vn);
+      step(s, ka, va, true);
+      load(s + 2, ka, va);
+      step(s + 1, kn, vn, true);
+    }
+    if (s + 1 < nsteps) {
+      load(s + 1, kn, vn);
+      step(s, ka, va, true);
+      step(s + 1, kn, vn, false);
+    } else {
+      step(s, ka, va, false);
+    }
+  }
+
+  // epilogue: query j is spread over lanes j, j+16, j+32, j+48; O carries
+  // the V scale
+  const float l_tot = sum_x32(sum_x16(l_run));
+  if (j >= nq) return;
+  const float inv = l_tot > 0.0f ? vsc / l_tot : 0.0f;
+  const float lse2 = l_tot > 0.0f ? m_run + log2_(l_tot) : kNegInf;
+  if (part < 0) {
+    uint16_t* op = a.o_decode + ((int64_t)qi * a.hq + h0 + j) * kHeadDim + 4 * q4;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const u32x2 w = {pack_bf16x2(o[db][0] * inv, o[db][1] * inv),
+                       pack_bf16x2(o[db][2] * inv, o[db][3] * inv)};
+      *(u32x2*)(op + 16 * db) = w;
+    }
+    if (q4 == 0 && a.lse_decode) a.lse_decode[(int64_t)qi * a.hq + h0 + j] = lse2 * kLn2;
+  } else {
+    const int pi = part + j * pstride;
+    float* pp = a.part_o + (int64_t)pi * kHeadDim + 4 * q4;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      *(f32x4*)(pp + 16 * db) = f32x4{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv,
+                                      o[db][3] * inv};
+    if (q4 == 0) a.part_lse[pi] = lse2;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Scheduling helpers
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int cu_slot_id() {
@@ -1144,6 +1370,22 @@ __global__ __launch_bounds__(256, 2) void pod_decode_kernel(KernelArgs a) {
   }
 }
 
+// FP8-cache decode kernel: one group of four units per workgroup, one unit
+// per wavefront (decode-only batches; every run path uses it).
+template <int KVM>
+__global__ __launch_bounds__(256, 2) void pod_decode_fp8_kernel(KernelArgs a) {
+  POD_LDS_OBJECTS
+  (void)s_info;
+  (void)ldsy;
+  const int wave = rfl(threadIdx.x >> 6);
+  const int d = blockIdx.x * kWavesPerWG + wave;
+  if (d < a.n_d) {
+    const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
+    decode_unit_fp8<KVM>(a, (cptr)a.d_items + d * D_FIELDS, ldsx + wave * kDecStepBytes);
+    if (a.trace && (threadIdx.x & 63) == 0) trace_unit(a, a.n_p + d, 1, d, cu_slot_id(), t0);
+  }
+}
+
 // Merge: one 16-lane group per (row, head) task, four tasks per wavefront.
 // Every load of a task -- its split LSEs (lane j holds splits j, j + 16, ..)
 // and its fp32 partial rows (16 lanes x 32 bytes = one 512-byte row) -- is
@@ -1343,6 +1585,18 @@ hipError_t launch_prefill(const KernelArgs& a, int kv_mode, int grid, hipStream_
 
 hipError_t launch_decode(const KernelArgs& a, int kv_mode, int grid, hipStream_t s) {
   POD_DISPATCH(pod_decode_kernel, 0)
+}
+
+hipError_t launch_decode_fp8(const KernelArgs& a, int kv_mode, int grid, hipStream_t s) {
+  switch (kv_mode) {
+    case KV_CONTIG:
+      hipLaunchKernelGGL(pod_decode_fp8_kernel<KV_CONTIG>, dim3(grid), dim3(256), 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL(pod_decode_fp8_kernel<KV_PAGED_WIDE>, dim3(grid), dim3(256), 0, s, a);
+      break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_merge(const KernelArgs& a, int grid, hipStream_t s) {

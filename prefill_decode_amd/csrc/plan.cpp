@@ -55,6 +55,16 @@ pod_status_t validate(const pod_attn_params_t* p, int32_t np, const int32_t* qo,
     return fail(err, POD_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %lld)", p->causal);
   if (!(std::isfinite(p->sm_scale) && p->sm_scale > 0.0f))
     return fail(err, POD_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
+  if (p->kv_dtype != POD_KV_BF16 && p->kv_dtype != POD_KV_FP8_E4M3)
+    return fail(err, POD_ERR_INVALID_ARGUMENT, "kv_dtype %lld invalid", p->kv_dtype);
+  if (p->kv_dtype == POD_KV_FP8_E4M3) {
+    if (np > 0)
+      return fail(err, POD_ERR_UNSUPPORTED, "FP8 KV caches are supported for decode-only "
+                  "batches (%lld prefill requests given)", np);
+    if (p->kv_layout == POD_KV_PAGED && p->page_size < 16)
+      return fail(err, POD_ERR_UNSUPPORTED, "FP8 KV caches need pages of >= 16 tokens (%lld)",
+                  p->page_size);
+  }
   if (np < 0 || nd < 0)
     return fail(err, POD_ERR_INVALID_ARGUMENT, "negative request count (%lld, %lld)", np, nd);
   if (np > 0 && (!qo || !pkv))
@@ -94,6 +104,8 @@ pod_status_t validate(const pod_attn_params_t* p, int32_t np, const int32_t* qo,
       return fail(err, POD_ERR_INVALID_ARGUMENT, "sched_mode %lld invalid", t->sched_mode);
     if (t->match_sequential != 0 && t->match_sequential != 1)
       return fail(err, POD_ERR_INVALID_ARGUMENT, "match_sequential must be 0 or 1");
+    if (p->kv_dtype == POD_KV_FP8_E4M3 && (t->flags & POD_FLAG_BATCHED_PREFILL))
+      return fail(err, POD_ERR_UNSUPPORTED, "the batched-prefill comparator reads bf16 caches only");
   }
   return POD_OK;
 }

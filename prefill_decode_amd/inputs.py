@@ -185,7 +185,8 @@ def _fp8_pool(seed: int, tag: int, shape, chunk: int):
         x[c0:c1] = rng.standard_normal((c1 - c0,) + tuple(shape[1:]), dtype=np.float32)
     axes = tuple(range(x.ndim - 2)) + (x.ndim - 1,)
     scale = (np.max(np.abs(x), axis=axes) / np.float32(FP8_MAX)).astype(np.float32)
-    return f32_to_fp8_e4m3_bits(x / scale[:, None]), scale
+    # x / scale of a head's largest |x| rounds to 448 give or take an ulp
+    return f32_to_fp8_e4m3_bits(np.clip(x / scale[:, None], -FP8_MAX, FP8_MAX)), scale
 
 
 def _normal_bf16(seed: int, tag: int, shape, chunk: Optional[int] = None) -> np.ndarray:
@@ -329,7 +330,8 @@ def make_batch_device(spec: BatchSpec, device="cuda", poison: bool = False) -> D
                                    dtype=torch.float32, device=device)
         dims = tuple(range(x.dim() - 2)) + (x.dim() - 1,)
         scale = (x.abs().amax(dim=dims) / FP8_MAX).float()
-        q = (x / scale[:, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        q = (x / scale[:, None]).clamp_(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn) \
+            .view(torch.uint8)
         del x
         return q, scale
 

@@ -67,6 +67,10 @@ OK, INV, UNS = 0, 1, 2
     (dict(layout=7), INV),
     (dict(causal=2), INV),
     (dict(qo=[3], kv=[1 << 25], dkv=[]), UNS),
+    (dict(kv_dtype=2), INV),                                # unknown dtype
+    (dict(kv_dtype=1), UNS),                                # FP8 cache with a prefill
+    (dict(kv_dtype=1, qo=[], kv=[]), OK),                   # FP8 decode-only
+    (dict(kv_dtype=1, qo=[], kv=[], page_size=8), UNS),     # FP8 needs pages >= 16
 ])
 def test_plan_validation(case, expect):
     p = B.make_params(case.get("hq", 8), case.get("hkv", 2), "paged",
@@ -76,6 +80,8 @@ def test_plan_validation(case, expect):
         p.kv_layout = case["layout"]
     if "causal" in case:
         p.causal = case["causal"]
+    if "kv_dtype" in case:
+        p.kv_dtype = case["kv_dtype"]
     st = _plan_status(p, case.get("qo", [4]), case.get("kv", [9]), case.get("dkv", [5]))
     assert st == expect, (st, B.last_error())
     if st != OK:
