@@ -53,6 +53,14 @@ DESCR = {
                 "(median 4096, sigma 1, cap 32768); paged 16",
     "batched": "batched multi-prefill: 32q/8kv d128; 4 chunks {128,256,512,640}@U[2048,8192] "
                "+ 192 decodes U[512,16384]; paged 16",
+    "llama2_7b_dec_bf16": "llama2-7b layer's decodes alone: 32q/32kv d128; 128 decodes @8192; "
+                          "paged 16; bf16 KV",
+    "llama2_7b_dec_fp8": "llama2-7b layer's decodes alone: 32q/32kv d128; 128 decodes @8192; "
+                         "paged 16; FP8 E4M3 KV, per-head scales",
+    "l70b_tp1_dec_bf16": "70b TP=1 layer's decodes alone: 64q/8kv d128; 256 decodes "
+                         "kv~lognormal; paged 16; bf16 KV",
+    "l70b_tp1_dec_fp8": "70b TP=1 layer's decodes alone: 64q/8kv d128; 256 decodes "
+                        "kv~lognormal; paged 16; FP8 E4M3 KV, per-head scales",
 }
 COPY_BYTES = 1 << 30          # calibration copy for the HBM byte counters
 PROFILES = os.path.join(ROOT, "profiles")
@@ -437,9 +445,10 @@ def pct(a, q):
 
 
 def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup, tuning_kw,
-                   paths=PATHS):
+                   paths=PATHS, spec=None):
     """Times every path on one workload; returns (runner, fields)."""
-    spec = inputs.config_spec(name, n_dec=n_dec)
+    if spec is None:
+        spec = inputs.config_spec(name, n_dec=n_dec)
     batch = inputs.make_batch_device(spec)
     counts = metrics.algorithmic_counts(spec)
     flags = B.FLAG_BATCHED_PREFILL if "batched" in paths else 0
@@ -452,7 +461,7 @@ def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup,
     for _ in range(5):
         t0 = time.perf_counter()
         p = B.plan_host(runner.params, spec.prefill_qo_len, spec.prefill_kv_len,
-                        spec.decode_kv_len, B.make_tuning(**tuning_kw))
+                        spec.decode_kv_len, B.make_tuning(flags=flags, **tuning_kw))
         warm.append((time.perf_counter() - t0) * 1e3)
         p.destroy()
     calls = {"fused": runner.run, "seq": runner.sequential_run}
@@ -472,7 +481,8 @@ def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup,
     roof_s = metrics.overlap_roofline_s(counts)
     info = runner.plan.info()
     f = {
-        "workload": DESCR.get(name, spec.name),
+        "workload": DESCR.get(spec.name, DESCR.get(name, spec.name)),
+        "kv_dtype": spec.kv_dtype,
         "fused_us": t_step * 1e6,
         "fused_us_p10_p90": [pct(t["fused"], 10), pct(t["fused"], 90)],
         "fused_kernel_us": t_kern * 1e6,
@@ -486,7 +496,7 @@ def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup,
         "achieved_tflops": counts["flops"] / t_step / 1e12,
         "achieved_hbm_gbs": counts["bytes"] / t_step / 1e9,
         "algorithmic": {"gflop": counts["flops"] / 1e9, "gbytes": counts["bytes"] / 1e9},
-        "traffic_bytes_per_launch": read_traffic(spec.name) if n_dec is None else None,
+        "traffic_bytes_per_launch": read_traffic(spec.name),
         "plan": {"first_call_ms": plan_first_ms, "host_warm_ms": float(np.median(warm)),
                  "prefill_items": info["prefill_items"], "decode_items": info["decode_items"],
                  "merge_tasks": info["merge_tasks"],
@@ -623,6 +633,18 @@ def main():
             per[key] = f
             del r, _rest
             torch.cuda.empty_cache()
+        # decode-only batches with a bf16 and an FP8 E4M3 cache (the FP8
+        # path's scope): the decodes of the llama2-7b and 70B-shaped layers
+        for name in ("llama2_7b", "l70b_tp1"):
+            for dt in ("bf16", "fp8_e4m3"):
+                spec_d = inputs.decode_only_spec(name, dt)
+                print(f"bench: {spec_d.name}", file=sys.stderr, flush=True)
+                r, *_rest, f = measure_config(torch, B, inputs, metrics, timer, name, None,
+                                              args.config_steps, 2, tuning_kw,
+                                              paths=("fused", "seq"), spec=spec_d)
+                per[spec_d.name] = f
+                del r, _rest
+                torch.cuda.empty_cache()
         out["per_config"] = per
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(batch, spec)

@@ -74,7 +74,10 @@ typedef enum { POD_KV_BF16 = 0, POD_KV_FP8_E4M3 = 1 } pod_kv_dtype_t;
  * pick their first role (every workgroup moves to the other queue when its
  * own runs dry, so all modes run every unit exactly once). */
 typedef enum {
-  /* The planner's choice (currently POD_SCHED_SPLIT). */
+  /* The planner's choice: for a batch of at most two fused units (prefill
+   * items + decode groups) per workgroup slot, POD_SCHED_COLOCATE with one
+   * workgroup per unit (POD_FLAG_ONE_UNIT_PER_WG); otherwise POD_SCHED_SPLIT
+   * with persistent workgroups. */
   POD_SCHED_AUTO = 0,
   /* Co-location on every CU: the CU's workgroups take roles in arrival
    * order (a per-CU ticket), the first prefill_quarters_per_cu / 4 of them
@@ -97,6 +100,14 @@ typedef enum {
                                  run) records one pod_trace_record_t per unit */
 #define POD_FLAG_BATCHED_PREFILL 0x2u  /* the plan also builds (and its workspace
                                  holds) the work list of pod_attn_batched_prefill_run */
+#define POD_FLAG_ONE_UNIT_PER_WG 0x4u  /* fused launch of one workgroup per unit
+                                 (prefill items + decode groups) instead of two
+                                 persistent workgroups per CU: each takes its role
+                                 as the scheduler mode says, runs one unit of it (or
+                                 of the other role when its own is exhausted) and
+                                 exits, the hardware refilling the slot -- the
+                                 launch shape of [POD] "Fuse prefill and decode
+                                 attention into one kernel" */
 
 typedef struct pod_attn_plan_s* pod_attn_plan_t;   /* opaque, library-owned */
 
@@ -152,6 +163,7 @@ typedef struct {
   int32_t seq_prefill_items, seq_decode_items, seq_merge_tasks;
   int32_t prefill_splits_max, decode_splits_max;
   int32_t wgs_per_cu, prefill_quarters_per_cu, sched_mode;
+  int32_t one_unit_per_wg;     /* 1: the fused launch runs one workgroup per unit */
   int32_t num_partials;
   int32_t trace_records;
   uint64_t workspace_bytes;

@@ -28,6 +28,7 @@ KV_BF16, KV_FP8_E4M3 = 0, 1
 SCHED_AUTO, SCHED_COLOCATE, SCHED_ORDERED, SCHED_SPLIT = 0, 1, 2, 3
 FLAG_TRACE = 0x1
 FLAG_BATCHED_PREFILL = 0x2
+FLAG_ONE_UNIT_PER_WG = 0x4
 
 # every function the header declares
 EXPORTED = ("pod_attn_plan", "pod_attn_plan_host", "pod_attn_run", "pod_attn_run_events",
@@ -66,7 +67,8 @@ class PlanInfo(C.Structure):
         "prefill_items", "decode_items", "decode_groups", "merge_tasks",
         "seq_prefill_items", "seq_decode_items", "seq_merge_tasks",
         "prefill_splits_max", "decode_splits_max", "wgs_per_cu",
-        "prefill_quarters_per_cu", "sched_mode", "num_partials", "trace_records")] + \
+        "prefill_quarters_per_cu", "sched_mode", "one_unit_per_wg", "num_partials",
+        "trace_records")] + \
         [("workspace_bytes", C.c_uint64)]
 
 

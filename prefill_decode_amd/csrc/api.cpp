@@ -95,6 +95,7 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   const int64_t slots = (int64_t)dev.num_cus * c.wgs_per_cu;
   const int64_t p_slots_coloc = std::max<int64_t>(1, (int64_t)dev.num_cus * c.prefill_quarters / 4);
   const bool small_prefill = sum_qo <= 1536;
+  c.one_unit = (t.flags & POD_FLAG_ONE_UNIT_PER_WG) != 0;
   if (c.sched_mode == POD_SCHED_ORDERED) {
     // one queue, prefill units first: each part has the whole GPU in turn,
     // so the lists are sized as the sequential kernels' are
@@ -108,6 +109,24 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
         small_prefill ? kFusedPrefillHalfItemsPerSlotSmall : kFusedPrefillHalfItemsPerSlotLarge;
     build_lists(pl->batch, dev, fused_p_slots, p_half_items, fused_d_waves,
                 kFusedDecodeUnitsPerWave, t.prefill_kv_splits, t.decode_kv_splits, &pl->fused);
+  }
+  // automatic launch shape (kOneUnitSlotsFactor): a small batch runs one
+  // workgroup per unit with per-CU tickets; its lists are rebuilt for the
+  // co-location share
+  if (t.sched_mode == POD_SCHED_AUTO && !c.one_unit &&
+      (int64_t)pl->fused.n_p() + pl->fused.n_groups() <= kOneUnitSlotsFactor * slots) {
+    c.sched_mode = POD_SCHED_COLOCATE;
+    c.one_unit = true;
+    if (t.prefill_quarters_per_cu < 0)
+      c.prefill_quarters = auto_prefill_quarters(pl->batch, c.wgs_per_cu, c.sched_mode);
+    const int64_t p_slots = std::max<int64_t>(1, (int64_t)dev.num_cus * c.prefill_quarters / 4);
+    const int64_t d_waves = std::max<int64_t>(
+        kWavesPerWG, (int64_t)dev.num_cus * (4 * c.wgs_per_cu - c.prefill_quarters));
+    build_lists(pl->batch, dev, small_prefill ? p_slots : slots,
+                small_prefill ? kFusedPrefillHalfItemsPerSlotSmall
+                              : kFusedPrefillHalfItemsPerSlotLarge,
+                d_waves, kFusedDecodeUnitsPerWave, t.prefill_kv_splits, t.decode_kv_splits,
+                &pl->fused);
   }
   // Sequential plan: each kernel has the whole GPU.
   pl->seq_is_fused = t.match_sequential == 1;
@@ -280,6 +299,7 @@ KernelArgs make_args(const pod_attn_plan_s* pl, const pod_attn_tensors_t* t, con
   a.wgs_per_cu = pl->choice.wgs_per_cu;
   a.prefill_quarters = pl->choice.prefill_quarters;
   a.sched_mode = pl->choice.sched_mode;
+  a.one_unit = pl->choice.one_unit ? 1 : 0;
   a.n_preq = (int32_t)pl->batch.qo.size();
   a.merge_splits = 0;
   a.merge_lse_scale = 1.0f;
@@ -428,9 +448,11 @@ pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t
   KernelArgs a = make_args(pl, t, w, pl->dl_fused);
   pick_counters(pl, kKindFused, stream, &a);
   if (pl->trace_records) a.trace = (pod_trace_record_t*)(pl->ws + pl->off_trace);
-  // persistent: wgs_per_cu workgroups per CU, fewer when there are fewer units
+  // persistent: wgs_per_cu workgroups per CU, fewer when there are fewer
+  // units; or one workgroup per unit
   const int64_t slots = (int64_t)pl->dev.num_cus * pl->choice.wgs_per_cu;
-  const int grid = (int)std::min<int64_t>(slots, (int64_t)w.n_p() + w.n_groups());
+  const int64_t units = (int64_t)w.n_p() + w.n_groups();
+  const int grid = (int)(a.one_unit ? units : std::min<int64_t>(slots, units));
   hipError_t e;
   if (before_fused && (e = hipEventRecord(before_fused, stream)) != hipSuccess)
     return hip_err(e, "hipEventRecord(before_fused)");
@@ -570,6 +592,7 @@ pod_status_t pod_attn_plan_info(pod_attn_plan_t pl, pod_attn_plan_info_t* out) {
   out->wgs_per_cu = pl->choice.wgs_per_cu;
   out->prefill_quarters_per_cu = pl->choice.prefill_quarters;
   out->sched_mode = pl->choice.sched_mode;
+  out->one_unit_per_wg = pl->choice.one_unit ? 1 : 0;
   out->num_partials = pl->n_partials;
   out->trace_records = pl->trace_records;
   out->workspace_bytes = pl->ws_bytes;

@@ -72,6 +72,7 @@ struct KernelArgs {
   int32_t causal;
   float scale_log2;       // sm_scale * log2(e)
   int32_t wgs_per_cu, prefill_quarters, sched_mode;
+  int32_t one_unit;       // 1: every workgroup runs one unit and exits
   int32_t n_preq;         // prefill requests: items with a larger KV request index are
                           // decode requests run through the prefill tile (batched prefill)
   // standalone merge (m_tasks == NULL): task t combines partials t * merge_splits

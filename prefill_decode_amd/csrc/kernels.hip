@@ -1237,7 +1237,7 @@ __device__ __forceinline__ void trace_unit(const KernelArgs& a, int rec, int rol
 // queue of that role: prefill tiles one workgroup at a time, decode units in
 // groups of four (one per wave).  When its queue runs dry it moves to the
 // other queue, so no slot idles while work is left.
-template <int KVM>
+template <int KVM, bool ONE = false>
 __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
   POD_LDS_OBJECTS
   const int tid = threadIdx.x;
@@ -1328,12 +1328,44 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
       }
     }
   };
-  if (role0 == 0) {
-    if (!prefill_phase()) decode_phase();
+  if constexpr (ONE) {
+    // one unit of the workgroup's role (or of the other one when its own is
+    // exhausted), then exit
+    __syncthreads();
+    if (tid == 0) {
+      int oe = 0, u = -1, g = -1;
+      const int q0 = (4 * xcc + (slot & 3)) % a.n_dq;
+      if (role0 == 0 && a.n_p > 0) u = claim_prefill(a, xcc, &oe);
+      if (u < 0 && a.n_d > 0) g = claim_decode_group(a, q0, &oe);
+      if (u < 0 && g < 0 && role0 != 0 && a.n_p > 0) u = claim_prefill(a, xcc, &oe);
+      s_info[2] = u;
+      s_info[3] = g;
+    }
+    __syncthreads();
+    const int u = rfl(s_info[2]), g = rfl(s_info[3]);
+    if (u >= 0) {
+      const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
+      prefill_tile<KVM>(a, (cptr)a.p_items + u * P_FIELDS, POD_PREFILL_BUFFERS);
+      if (a.trace && tid == 0) trace_unit(a, u, 0, u, slot, t0);
+    } else if (g >= 0) {
+      POD_DECODE_BUFFERS(wave)
+      const int du = g * kWavesPerWG + wave;
+      if (du < a.n_d) {
+        const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
+        int ticket;
+        decode_unit<KVM>(a, (cptr)a.d_items + du * D_FIELDS, db0, db1, nullptr, ticket);
+        if (a.trace && lane == 0) trace_unit(a, a.n_p + du, 1, du, slot, t0);
+      }
+    }
+    finish_launch(a, &s_info[4]);
   } else {
-    if (!decode_phase()) prefill_phase();
+    if (role0 == 0) {
+      if (!prefill_phase()) decode_phase();
+    } else {
+      if (!decode_phase()) prefill_phase();
+    }
+    finish_launch(a, &s_info[4]);
   }
-  finish_launch(a, &s_info[4]);
 }
 
 template <int KVM, bool BP = false>
@@ -1557,8 +1589,26 @@ hipError_t scratch_address(int device, void** out) {
   }                                                                                      \
   return hipGetLastError();
 
+template <bool ONE>
+struct FusedK {
+  template <int KVM>
+  static void launch(int grid, hipStream_t s, const KernelArgs& a) {
+    hipLaunchKernelGGL((pod_fused_kernel<KVM, ONE>), dim3(grid), dim3(256), 0, s, a);
+  }
+};
+
 hipError_t launch_fused(const KernelArgs& a, int kv_mode, int grid, hipStream_t s) {
-  POD_DISPATCH(pod_fused_kernel, 0)
+  auto go = [&](auto k) {
+    using K = decltype(k);
+    switch (kv_mode) {
+      case KV_CONTIG: K::template launch<KV_CONTIG>(grid, s, a); break;
+      case KV_PAGED_WIDE: K::template launch<KV_PAGED_WIDE>(grid, s, a); break;
+      default: K::template launch<KV_PAGED_NARROW>(grid, s, a); break;
+    }
+  };
+  if (a.one_unit) go(FusedK<true>{});
+  else go(FusedK<false>{});
+  return hipGetLastError();
 }
 
 template <bool BP>

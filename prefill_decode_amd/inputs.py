@@ -122,6 +122,15 @@ def config_spec(name: str, n_dec: Optional[int] = None) -> BatchSpec:
     raise ValueError(f"unknown config {name!r}")
 
 
+def decode_only_spec(name: str, kv_dtype: str = "bf16") -> BatchSpec:
+    """The decodes of workload ``name`` alone (its prefill dropped), with a
+    bf16 or an FP8 E4M3 cache (the FP8 path's scope is decode-only)."""
+    base = config_spec(name)
+    suffix = "_dec_fp8" if kv_dtype == "fp8_e4m3" else "_dec_bf16"
+    return replace(base, name=base.name + suffix, prefill_qo_len=(), prefill_kv_len=(),
+                   kv_dtype=kv_dtype)
+
+
 def custom_spec(name: str, num_qo_heads: int, num_kv_heads: int,
                 prefill: Sequence[Tuple[int, int]], decode_kv: Sequence[int],
                 seed: int, **kw) -> BatchSpec:

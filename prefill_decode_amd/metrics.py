@@ -9,6 +9,7 @@ indices as int32, and only the visible (query, key) pairs:
 
 Re-reads of K/V by several prefill tiles, split partials, masked MFMA work on
 diagonal tiles and the padding of decode rows to 16 are overheads, not counted.
+An FP8 KV cache counts one byte per K or V element plus its per-head scales.
 """
 
 import numpy as np
@@ -31,13 +32,20 @@ def algorithmic_counts(b) -> dict:
     ps = get("page_size")
     rows_p, rows_d = float(np.sum(qo)), float(len(dkv))
 
+    try:
+        kv_elem = 1.0 if get("kv_dtype") == "fp8_e4m3" else 2.0
+    except (AttributeError, KeyError):
+        kv_elem = 2.0
+
     def part_bytes(rows, kv_tokens, pages):
         qo_b = rows * hq * d * 2 * 2 + rows * hq * 4          # Q + O (bf16) + LSE
-        kv_b = kv_tokens * hkv * d * 2 * 2                    # K + V (bf16)
+        kv_b = kv_tokens * hkv * d * kv_elem * 2              # K + V
         return qo_b + kv_b + (pages * 4 if paged else 0.0)
 
     bp = part_bytes(rows_p, float(np.sum(pkv)), float(np.sum(np.ceil(pkv / ps))))
     bd = part_bytes(rows_d, float(np.sum(dkv)), float(np.sum(np.ceil(dkv / ps))))
+    if kv_elem == 1.0:
+        bd += 2 * hkv * 4                                     # K and V scales
     fp = 4.0 * d * hq * pairs_p
     fd = 4.0 * d * hq * pairs_d
     return {"flops": fp + fd, "bytes": bp + bd, "flops_prefill": fp, "flops_decode": fd,

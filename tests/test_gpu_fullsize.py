@@ -83,7 +83,11 @@ def test_fullsize_every_row(name):
     tunings = ()
     if name == "llama3_8b":
         tunings = (("colocate", B.make_tuning(sched_mode=B.SCHED_COLOCATE)),
-                   ("ordered", B.make_tuning(sched_mode=B.SCHED_ORDERED)))
+                   ("ordered", B.make_tuning(sched_mode=B.SCHED_ORDERED)),
+                   ("one-unit split", B.make_tuning(sched_mode=B.SCHED_SPLIT,
+                                                    flags=B.FLAG_ONE_UNIT_PER_WG)),
+                   ("one-unit colocate", B.make_tuning(sched_mode=B.SCHED_COLOCATE,
+                                                       flags=B.FLAG_ONE_UNIT_PER_WG)))
     _every_row(inputs.config_spec(name), ("fused", "seq", "streams", "batched"), tunings)
 
 
@@ -132,9 +136,13 @@ def test_scheduler_traces():
     say(f"  co-locate: CUs used {len(slots)}, running prefill and decode at once {both}")
     assert len(slots) == 256
     assert both >= 0.5 * len(slots)
-    # CU partition (the default): about q/8 of the CUs start on prefill, and
-    # the prefill and decode units overlap in time across the GPU
+    # the automatic choice for this layer: one workgroup per unit with
+    # per-CU tickets (every unit once, outputs checked)
     info, tr = _trace(spec, bd, B.SCHED_AUTO, ref)
+    assert info["sched_mode"] == B.SCHED_COLOCATE and info["one_unit_per_wg"] == 1
+    # CU partition: about q/8 of the CUs start on prefill, and the prefill and
+    # decode units overlap in time across the GPU
+    info, tr = _trace(spec, bd, B.SCHED_SPLIT, ref)
     assert info["sched_mode"] == B.SCHED_SPLIT
     q = info["prefill_quarters_per_cu"]
     role, slot, t0, t1 = tr[:, 2], tr[:, 1], tr[:, 4], tr[:, 5]

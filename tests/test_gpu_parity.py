@@ -77,6 +77,14 @@ def test_edge_cases(spec):
     _check(spec)
 
 
+@pytest.mark.parametrize("spec", reduced_specs() + edge_specs()[:4], ids=lambda s: s.name)
+def test_one_unit_per_workgroup(spec):
+    # the fused launch of one workgroup per unit (split and co-located roles)
+    for mode in (B.SCHED_SPLIT, B.SCHED_COLOCATE):
+        _check(spec, B.make_tuning(sched_mode=mode, flags=B.FLAG_ONE_UNIT_PER_WG),
+               paths=("fused",))
+
+
 @pytest.mark.parametrize("spec", [inputs.config_spec("tiny"), reduced_specs()[1]],
                          ids=lambda s: s.name)
 def test_sharp_scale(spec):
@@ -115,11 +123,14 @@ def test_fused_equals_matched_sequential_bitwise_and_sched_modes():
     b = inputs.make_batch_host(spec)
     ref = oracle.batch_attention(b)
     results = []
-    for mode in (B.SCHED_AUTO, B.SCHED_COLOCATE, B.SCHED_ORDERED, B.SCHED_SPLIT):
+    for mode, flags in ((B.SCHED_AUTO, 0), (B.SCHED_COLOCATE, 0), (B.SCHED_ORDERED, 0),
+                        (B.SCHED_SPLIT, 0), (B.SCHED_SPLIT, B.FLAG_ONE_UNIT_PER_WG),
+                        (B.SCHED_COLOCATE, B.FLAG_ONE_UNIT_PER_WG),
+                        (B.SCHED_ORDERED, B.FLAG_ONE_UNIT_PER_WG)):
         for q in (1, 4, 7):
-            say(f"[bitwise] mode={mode} quarters={q}")
+            say(f"[bitwise] mode={mode} flags={flags} quarters={q}")
             t = B.make_tuning(match_sequential=1, sched_mode=mode, prefill_quarters_per_cu=q,
-                              prefill_kv_splits=2, decode_kv_splits=3)
+                              prefill_kv_splits=2, decode_kv_splits=3, flags=flags)
             r = B.BatchRunner(b, t)
             f1 = run_path(r, "fused")
             f2 = run_path(r, "fused")

@@ -224,12 +224,22 @@ def test_small_prefill_regime_accounts_for_colocated_decode():
 
 
 def test_proportional_mix():
-    q = {n: _spec_lists(inputs.config_spec(n)).info()["prefill_quarters_per_cu"]
-         for n in inputs.CONFIG_NAMES}
-    # default (CU partition): 3..6 eighths of the CUs start on prefill
+    info = {n: _spec_lists(inputs.config_spec(n)).info() for n in inputs.CONFIG_NAMES}
+    q = {n: i["prefill_quarters_per_cu"] for n, i in info.items()}
+    for n, i in info.items():
+        # automatic launch shape: one workgroup per unit (co-located roles)
+        # for at most two fused units per workgroup slot, else persistent
+        # CU partition
+        small = i["prefill_items"] + i["decode_groups"] <= 2 * 512
+        assert i["one_unit_per_wg"] == int(small), n
+        if small:
+            assert i["sched_mode"] == B.SCHED_COLOCATE and 1 <= q[n] <= 7, n
+        else:
+            # CU partition: 3..6 eighths of the CUs start on prefill
+            assert i["sched_mode"] == B.SCHED_SPLIT and 3 <= q[n] <= 6, n
+    assert info["llama3_8b"]["one_unit_per_wg"] == 1 and info["tiny"]["one_unit_per_wg"] == 1
     assert q["llama2_7b"] == 3              # decode-heavy MHA: smallest prefill share
     assert q["l70b_tp1"] >= 3               # large prefill: about half or more
-    assert all(3 <= q[n] <= 6 for n in q)
     assert _spec_lists(inputs.config_spec("l70b_tp1"), sched_mode=B.SCHED_SPLIT).info()[
         "sched_mode"] == B.SCHED_SPLIT
     assert _spec_lists(inputs.config_spec("l70b_tp1")).info()["sched_mode"] == B.SCHED_SPLIT
