@@ -61,6 +61,9 @@ DESCR = {
                          "kv~lognormal; paged 16; bf16 KV",
     "l70b_tp1_dec_fp8": "70b TP=1 layer's decodes alone: 64q/8kv d128; 256 decodes "
                         "kv~lognormal; paged 16; FP8 E4M3 KV, per-head scales",
+    "l70b_prefix": "70b TP=1 layer, shared-prefix decodes: 64q/8kv d128; 128 decodes in 16 "
+                   "groups of 8 sharing a 2048-token prefix + own U[64,1024]; paged 16; "
+                   "fused = packed (PAT-style), sequential = unshared decode",
 }
 COPY_BYTES = 1 << 30          # calibration copy for the HBM byte counters
 PROFILES = os.path.join(ROOT, "profiles")
@@ -460,8 +463,16 @@ def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup,
     warm = []
     for _ in range(5):
         t0 = time.perf_counter()
-        p = B.plan_host(runner.params, spec.prefill_qo_len, spec.prefill_kv_len,
-                        spec.decode_kv_len, B.make_tuning(flags=flags, **tuning_kw))
+        if spec.prefix_groups:
+            grp = np.full(spec.num_decode, -1, dtype=np.int32)
+            for gi, (m, _pl) in enumerate(spec.prefix_groups):
+                grp[list(m)] = gi
+            p = B.plan_shared_prefix_host(runner.params, spec.decode_kv_len, grp,
+                                          [pl_ for _m, pl_ in spec.prefix_groups],
+                                          B.make_tuning(**tuning_kw))
+        else:
+            p = B.plan_host(runner.params, spec.prefill_qo_len, spec.prefill_kv_len,
+                            spec.decode_kv_len, B.make_tuning(flags=flags, **tuning_kw))
         warm.append((time.perf_counter() - t0) * 1e3)
         p.destroy()
     calls = {"fused": runner.run, "seq": runner.sequential_run}
@@ -496,6 +507,7 @@ def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup,
         "achieved_tflops": counts["flops"] / t_step / 1e12,
         "achieved_hbm_gbs": counts["bytes"] / t_step / 1e9,
         "algorithmic": {"gflop": counts["flops"] / 1e9, "gbytes": counts["bytes"] / 1e9},
+        "achieved_hbm_gbs_kernel": counts["bytes"] / t_kern / 1e9,
         "traffic_bytes_per_launch": read_traffic(spec.name),
         "plan": {"first_call_ms": plan_first_ms, "host_warm_ms": float(np.median(warm)),
                  "prefill_items": info["prefill_items"], "decode_items": info["decode_items"],
@@ -645,6 +657,18 @@ def main():
                 per[spec_d.name] = f
                 del r, _rest
                 torch.cuda.empty_cache()
+        # decode-only batch with shared prefixes: the packed path (fused
+        # field) against the unshared decode of the same batch (sequential)
+        spec_p = inputs.config_spec("l70b_prefix")
+        print(f"bench: {spec_p.name}", file=sys.stderr, flush=True)
+        r, *_rest, f = measure_config(torch, B, inputs, metrics, timer, spec_p.name, None,
+                                      args.config_steps, 2, tuning_kw,
+                                      paths=("fused", "seq"), spec=spec_p)
+        f["algorithmic"]["gbytes_unshared"] = metrics.algorithmic_counts(spec_p)[
+            "bytes_unshared"] / 1e9
+        per[spec_p.name] = f
+        del r, _rest
+        torch.cuda.empty_cache()
         out["per_config"] = per
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(batch, spec)

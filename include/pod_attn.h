@@ -260,6 +260,45 @@ pod_status_t pod_attn_plan_host(const pod_attn_params_t* params,
                                 const pod_device_desc_t* device,
                                 pod_attn_plan_t* out_plan);
 
+/* Plans a decode-only batch whose requests share KV prefixes, the
+ * pack-forward-merge of [PAT] (abstract: queries packed by shared prefix so
+ * that the prefix's KV is loaded once; KV splitting; a final online-softmax
+ * merge).
+ *   decode_kv_len: host int32 [num_decode] (>= 1)
+ *   prefix_group:  host int32 [num_decode]: the request's group in
+ *                  [0, num_groups), or -1 (no shared prefix)
+ *   prefix_len:    host int32 [num_groups]: tokens every member of the group
+ *                  shares -- a whole number of pages, >= 1, no longer than any
+ *                  member's kv_len.  The members' page tables must hold the
+ *                  same pages for these tokens (the kernel reads the prefix
+ *                  through the group's first member's table).
+ * For each KV head, the rows of up to 16 / min(Hq/Hkv, 16) members are packed
+ * into one 16-row decode tile over the prefix; each member's own keys run as
+ * ordinary units; every (request, head) result is merged by log-sum-exp.
+ * pod_attn_run runs this packed path; pod_attn_sequential_run and
+ * pod_attn_streams_run run the ordinary (unshared) decode of the same batch,
+ * the baseline.  Workspace, ownership and errors as pod_attn_plan, plus
+ * POD_ERR_UNSUPPORTED for a contiguous or FP8 cache or the batched-prefill
+ * flag, and POD_ERR_INVALID_ARGUMENT for group ids or prefix lengths out of
+ * range. */
+pod_status_t pod_attn_plan_shared_prefix(const pod_attn_params_t* params, int32_t num_decode,
+                                         const int32_t* decode_kv_len,
+                                         const int32_t* prefix_group, int32_t num_groups,
+                                         const int32_t* prefix_len,
+                                         const pod_attn_tuning_t* tuning, void* workspace,
+                                         size_t workspace_bytes, size_t* workspace_needed,
+                                         hipStream_t stream, pod_attn_plan_t* out_plan);
+
+/* pod_attn_plan_shared_prefix without a GPU (host inspection, as
+ * pod_attn_plan_host); the plan cannot run. */
+pod_status_t pod_attn_plan_shared_prefix_host(const pod_attn_params_t* params,
+                                              int32_t num_decode, const int32_t* decode_kv_len,
+                                              const int32_t* prefix_group, int32_t num_groups,
+                                              const int32_t* prefix_len,
+                                              const pod_attn_tuning_t* tuning,
+                                              const pod_device_desc_t* device,
+                                              pod_attn_plan_t* out_plan);
+
 /* pod_attn_plan for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the plan's workspace is a static 128 MiB device array of the library, one
@@ -356,7 +395,8 @@ pod_status_t pod_attn_plan_info(pod_attn_plan_t plan, pod_attn_plan_info_t* out)
  * which: 0 fused prefill items (8 int32 each), 1 fused decode items (8 each),
  * 2 fused merge tasks (4 each), 3/4/5 the sequential lists, 6/7 the fused /
  * sequential prefill pool offsets (num_xcds + 1 each), 8/9/10 the
- * batched-prefill items, merge tasks and pool offsets.  Item fields are
+ * batched-prefill items, merge tasks and pool offsets, 11 the group members
+ * of a shared-prefix plan (decode indices).  Item fields are
  * documented in plan.h of the sources.  Errors: POD_ERR_INVALID_ARGUMENT. */
 pod_status_t pod_attn_plan_export(pod_attn_plan_t plan, int32_t which,
                                   int32_t* dst, size_t n, size_t* count);

@@ -36,7 +36,8 @@ EXPORTED = ("pod_attn_plan", "pod_attn_plan_host", "pod_attn_run", "pod_attn_run
             "pod_attn_merge",
             "pod_attn_plan_info", "pod_attn_plan_export", "pod_attn_read_trace",
             "pod_attn_plan_destroy", "pod_attn_last_error", "pod_attn_probe_hwid",
-            "pod_attn_probe_read_bw", "pod_attn_plan_scratch")
+            "pod_attn_probe_read_bw", "pod_attn_plan_scratch", "pod_attn_plan_shared_prefix",
+            "pod_attn_plan_shared_prefix_host")
 
 
 class PodError(RuntimeError):
@@ -102,6 +103,16 @@ def lib():
         L.pod_attn_plan.argtypes = [C.POINTER(Params), C.c_int32, i32p, i32p, C.c_int32, i32p,
                                     C.POINTER(Tuning), C.c_void_p, C.c_size_t,
                                     C.POINTER(C.c_size_t), C.c_void_p, C.POINTER(C.c_void_p)]
+        L.pod_attn_plan_shared_prefix.argtypes = [C.POINTER(Params), C.c_int32, i32p, i32p,
+                                                  C.c_int32, i32p, C.POINTER(Tuning),
+                                                  C.c_void_p, C.c_size_t,
+                                                  C.POINTER(C.c_size_t), C.c_void_p,
+                                                  C.POINTER(C.c_void_p)]
+        L.pod_attn_plan_shared_prefix_host.argtypes = [C.POINTER(Params), C.c_int32, i32p,
+                                                       i32p, C.c_int32, i32p,
+                                                       C.POINTER(Tuning),
+                                                       C.POINTER(DeviceDesc),
+                                                       C.POINTER(C.c_void_p)]
         L.pod_attn_plan_scratch.argtypes = [C.POINTER(Params), C.c_int32, i32p, i32p,
                                             C.c_int32, i32p, C.POINTER(Tuning), C.c_void_p,
                                             C.POINTER(C.c_void_p)]
@@ -255,6 +266,41 @@ def plan(params: Params, prefill_qo: Sequence[int], prefill_kv: Sequence[int],
     return Plan(h.value, workspace=ws)
 
 
+def plan_shared_prefix_host(params: Params, decode_kv: Sequence[int],
+                            prefix_group: Sequence[int], prefix_len: Sequence[int],
+                            tuning: Optional[Tuning] = None, num_cus: int = 256,
+                            num_xcds: int = 8) -> Plan:
+    """Shared-prefix plan without a GPU (host inspection); it cannot run."""
+    dk, pg, pln = _i32(decode_kv), _i32(prefix_group), _i32(prefix_len)
+    h = C.c_void_p(0)
+    dev = DeviceDesc(num_cus, num_xcds)
+    _check(lib().pod_attn_plan_shared_prefix_host(C.byref(params), len(dk), _ptr(dk), _ptr(pg),
+                                                  len(pln), _ptr(pln),
+                                                  C.byref(tuning) if tuning else None,
+                                                  C.byref(dev), C.byref(h)))
+    return Plan(h.value)
+
+
+def plan_shared_prefix(params: Params, decode_kv: Sequence[int], prefix_group: Sequence[int],
+                       prefix_len: Sequence[int], tuning: Optional[Tuning] = None,
+                       device="cuda", stream=None) -> Plan:
+    """Shared-prefix (packed) decode plan; allocates its torch workspace."""
+    import torch
+    dk, pg, pln = _i32(decode_kv), _i32(prefix_group), _i32(prefix_len)
+    need = C.c_size_t(0)
+    s = _stream(stream)
+    tp = C.byref(tuning) if tuning else None
+    _check(lib().pod_attn_plan_shared_prefix(C.byref(params), len(dk), _ptr(dk), _ptr(pg),
+                                             len(pln), _ptr(pln), tp, None, 0, C.byref(need),
+                                             s, None))
+    ws = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=device)
+    h = C.c_void_p(0)
+    _check(lib().pod_attn_plan_shared_prefix(C.byref(params), len(dk), _ptr(dk), _ptr(pg),
+                                             len(pln), _ptr(pln), tp, C.c_void_p(ws.data_ptr()),
+                                             ws.numel(), C.byref(need), s, C.byref(h)))
+    return Plan(h.value, workspace=ws)
+
+
 def plan_scratch(params: Params, prefill_qo: Sequence[int], prefill_kv: Sequence[int],
                  decode_kv: Sequence[int], tuning: Optional[Tuning] = None,
                  stream=None) -> Plan:
@@ -382,8 +428,19 @@ class BatchRunner:
                                        device=device)
         self.lse_decode = torch.empty(self.q_decode.shape[0], hq, dtype=torch.float32,
                                       device=device)
-        self.plan = plan(self.params, b["prefill_qo_len"], b["prefill_kv_len"],
-                         b["decode_kv_len"], tuning, device=device)
+        if b.get("prefix_groups"):
+            # decode-only batch with shared prefixes: the packed plan
+            nd = len(b["decode_kv_len"])
+            grp = np.full(nd, -1, dtype=np.int32)
+            plen = []
+            for gi, (members, pl_) in enumerate(b["prefix_groups"]):
+                grp[list(members)] = gi
+                plen.append(pl_)
+            self.plan = plan_shared_prefix(self.params, b["decode_kv_len"], grp, plen, tuning,
+                                           device=device)
+        else:
+            self.plan = plan(self.params, b["prefill_qo_len"], b["prefill_kv_len"],
+                             b["decode_kv_len"], tuning, device=device)
         self.tensors = make_tensors(self.q_prefill, self.q_decode, self.k, self.v,
                                     self.kv_indptr, self.page_indptr, self.page_indices,
                                     self.o_prefill, self.o_decode, self.lse_prefill,

@@ -44,6 +44,9 @@ struct pod_attn_plan_s {
   WorkLists bp;                // batched-prefill comparator (POD_FLAG_BATCHED_PREFILL)
   bool seq_is_fused = false;
   bool has_bp = false;
+  bool has_prefix = false;     // shared-prefix plan: `fused` holds the packed lists
+  std::vector<int32_t> members;   // shared-prefix plan: decode index of each group member
+  size_t off_members = 0;
   int32_t n_partials = 0;
   int32_t trace_records = 0;
   // workspace layout (bytes)
@@ -62,6 +65,8 @@ struct pod_attn_plan_s {
 };
 
 namespace {
+
+void layout_workspace(pod_attn_plan_s* pl);
 
 pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32_t* qo,
                         const int32_t* pkv, int32_t nd, const int32_t* dkv,
@@ -140,10 +145,15 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   if (pl->has_bp)
     build_lists(pl->batch, dev, slots, kSeqPrefillHalfItemsPerSlot, 0, 1, t.prefill_kv_splits, 0,
                 &pl->bp, /*decodes_as_prefill=*/true);
-  pl->n_partials = std::max(std::max(pl->fused.n_partials, sq.n_partials), pl->bp.n_partials);
   pl->trace_records = (t.flags & POD_FLAG_TRACE) ? pl->fused.n_p() + pl->fused.n_d() : 0;
+  layout_workspace(pl);
+  return POD_OK;
+}
 
-  // workspace layout
+// Workspace layout of a plan: counters, the work lists, trace, partials.
+void layout_workspace(pod_attn_plan_s* pl) {
+  const WorkLists& sq = pl->seq_is_fused ? pl->fused : pl->seq;
+  pl->n_partials = std::max(std::max(pl->fused.n_partials, sq.n_partials), pl->bp.n_partials);
   size_t off = 0;
   pl->off_counters = off;
   off = align_up(off + kCounterInts * sizeof(int32_t));
@@ -159,6 +169,8 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   if (pl->seq_is_fused) pl->dl_seq = pl->dl_fused;
   else place(pl->seq, pl->dl_seq);
   if (pl->has_bp) place(pl->bp, pl->dl_bp);
+  pl->off_members = off;
+  off = align_up(off + pl->members.size() * sizeof(int32_t));
   pl->off_trace = off;
   off = align_up(off + (size_t)pl->trace_records * sizeof(pod_trace_record_t));
   pl->off_part_lse = off;
@@ -166,7 +178,6 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   pl->off_part_o = off;
   off = align_up(off + (size_t)pl->n_partials * kHeadDim * sizeof(float));
   pl->ws_bytes = off;
-  return POD_OK;
 }
 
 pod_status_t query_device(pod_device_desc_t* dev, int* device) {
@@ -273,6 +284,8 @@ KernelArgs make_args(const pod_attn_plan_s* pl, const pod_attn_tensors_t* t, con
   a.lse_decode = t->lse_decode;
   a.k_scale = t->k_scale;
   a.v_scale = t->v_scale;
+  a.d_members = (const int32_t*)(pl->ws + pl->off_members);
+  a.pack_rpr = std::min(p.num_qo_heads / p.num_kv_heads, kDecodeRows);
   a.part_o = (float*)(pl->ws + pl->off_part_o);
   a.part_lse = (float*)(pl->ws + pl->off_part_lse);
   a.p_items = (const int32_t*)(pl->ws + dl.p_items);
@@ -310,6 +323,103 @@ pod_status_t launch_merge_of(const KernelArgs& a, const WorkLists& w, hipStream_
   if (w.n_m() == 0) return POD_OK;
   hipError_t e = launch_merge(a, (w.n_m() + kMergeTasksPerWG - 1) / kMergeTasksPerWG, stream);
   return e == hipSuccess ? POD_OK : hip_err(e, "merge kernel launch");
+}
+
+// The device half of a plan call: reports the workspace size, or takes the
+// caller's workspace, zeroes the counters and uploads the work lists on
+// `stream`.  Consumes `pl` (deleted unless it becomes *out_plan).
+// A decode-only plan for queries packed by shared prefix ([PAT] abstract):
+// the ordinary decode lists (the unshared baseline) for the sequential and
+// streams paths, the packed lists in place of the fused ones.
+pod_status_t build_prefix_plan(const pod_attn_params_t* params, int32_t nd, const int32_t* dkv,
+                               const int32_t* prefix_group, int32_t num_groups,
+                               const int32_t* prefix_len, const pod_attn_tuning_t* tuning,
+                               const pod_device_desc_t& dev, pod_attn_plan_s* pl) {
+  if (!params) return set_err(POD_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (params->kv_layout != POD_KV_PAGED || params->kv_dtype != POD_KV_BF16)
+    return set_err(POD_ERR_UNSUPPORTED, "shared-prefix plans need a paged bf16 cache");
+  if (tuning && (tuning->flags & POD_FLAG_BATCHED_PREFILL))
+    return set_err(POD_ERR_UNSUPPORTED, "no batched-prefill comparator for shared-prefix plans");
+  if (num_groups < 0 || (num_groups > 0 && !prefix_len) || (nd > 0 && (!prefix_group || !dkv)))
+    return set_err(POD_ERR_INVALID_ARGUMENT, "prefix group arrays are NULL or num_groups < 0");
+  std::vector<int32_t> group_of(prefix_group, prefix_group + std::max(0, nd));
+  std::vector<int32_t> plen(prefix_len, prefix_len + num_groups);
+  for (int32_t i = 0; i < nd; ++i) {
+    const int32_t gi = group_of[i];
+    if (gi < -1 || gi >= num_groups)
+      return set_err(POD_ERR_INVALID_ARGUMENT, "prefix_group entry out of range");
+    if (gi >= 0 && (plen[gi] < 1 || params->page_size < 1 || plen[gi] % params->page_size != 0 ||
+                    plen[gi] > dkv[i]))
+      return set_err(POD_ERR_INVALID_ARGUMENT,
+                     "a shared prefix must be whole pages, >= 1 token and no longer than any "
+                     "member's kv_len");
+  }
+  pod_attn_tuning_t t{};
+  t.prefill_quarters_per_cu = -1;
+  if (tuning) t = *tuning;
+  t.match_sequential = 0;
+  t.flags &= ~(POD_FLAG_TRACE | POD_FLAG_ONE_UNIT_PER_WG);
+  try {
+    pod_status_t st = build_plan(params, 0, nullptr, nullptr, nd, dkv, &t, dev, pl);
+    if (st != POD_OK) return st;
+    const int64_t waves = (int64_t)dev.num_cus * pl->choice.wgs_per_cu * kWavesPerWG;
+    build_prefix_lists(pl->batch, group_of, plen, waves, t.decode_kv_splits, &pl->fused,
+                       &pl->members);
+    pl->has_prefix = true;
+    pl->trace_records = 0;
+    layout_workspace(pl);
+  } catch (const std::exception& ex) {
+    return set_err(POD_ERR_INTERNAL, ex.what());
+  }
+  return POD_OK;
+}
+
+pod_status_t finish_device_plan(pod_attn_plan_s* pl, int device, void* workspace,
+                                size_t workspace_bytes, size_t* workspace_needed,
+                                hipStream_t stream, pod_attn_plan_t* out_plan) {
+  pod_status_t st;
+  if (workspace_needed) *workspace_needed = pl->ws_bytes;
+  if (!workspace) {
+    delete pl;
+    return POD_OK;
+  }
+  if (!out_plan) {
+    delete pl;
+    return set_err(POD_ERR_INVALID_ARGUMENT, "out_plan is NULL");
+  }
+  if (workspace_bytes < pl->ws_bytes) {
+    char buf[128];
+    std::snprintf(buf, sizeof(buf), "workspace has %zu bytes, plan needs %zu", workspace_bytes,
+                  pl->ws_bytes);
+    delete pl;
+    return set_err(POD_ERR_WORKSPACE_TOO_SMALL, buf);
+  }
+  if (!aligned16(workspace)) {
+    delete pl;
+    return set_err(POD_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
+  }
+  pl->ws = (char*)workspace;
+  pl->device = device;
+  hipError_t e = hipMemsetAsync(pl->ws + pl->off_counters, 0, kCounterInts * sizeof(int32_t), stream);
+  if (e != hipSuccess) {
+    delete pl;
+    return hip_err(e, "hipMemsetAsync(counters)");
+  }
+  auto up = [&](const WorkLists& w, const DevLists& d) -> pod_status_t {
+    pod_status_t s2;
+    if ((s2 = upload(pl->ws, d.p_items, w.p_items, stream)) != POD_OK) return s2;
+    if ((s2 = upload(pl->ws, d.d_items, w.d_items, stream)) != POD_OK) return s2;
+    return upload(pl->ws, d.m_tasks, w.m_tasks, stream);
+  };
+  if ((st = up(pl->fused, pl->dl_fused)) != POD_OK ||
+      (!pl->seq_is_fused && (st = up(pl->seq, pl->dl_seq)) != POD_OK) ||
+      (pl->has_bp && (st = up(pl->bp, pl->dl_bp)) != POD_OK) ||
+      (st = upload(pl->ws, pl->off_members, pl->members, stream)) != POD_OK) {
+    delete pl;
+    return st;
+  }
+  *out_plan = pl;
+  return POD_OK;
 }
 
 }  // namespace
@@ -368,42 +478,51 @@ pod_status_t pod_attn_plan(const pod_attn_params_t* params, int32_t num_prefill,
     delete pl;
     return st;
   }
-  if (workspace_needed) *workspace_needed = pl->ws_bytes;
-  if (!workspace) {
+  return finish_device_plan(pl, device, workspace, workspace_bytes, workspace_needed, stream,
+                            out_plan);
+}
+
+pod_status_t pod_attn_plan_shared_prefix(const pod_attn_params_t* params, int32_t num_decode,
+                                         const int32_t* decode_kv_len,
+                                         const int32_t* prefix_group, int32_t num_groups,
+                                         const int32_t* prefix_len,
+                                         const pod_attn_tuning_t* tuning, void* workspace,
+                                         size_t workspace_bytes, size_t* workspace_needed,
+                                         hipStream_t stream, pod_attn_plan_t* out_plan) {
+  if (out_plan) *out_plan = nullptr;
+  if (!workspace_needed && !workspace)
+    return set_err(POD_ERR_INVALID_ARGUMENT, "workspace and workspace_needed are both NULL");
+  pod_device_desc_t dev;
+  int device = -1;
+  pod_status_t st = query_device(&dev, &device);
+  if (st != POD_OK) return st;
+  pod_attn_plan_s* pl = new (std::nothrow) pod_attn_plan_s();
+  if (!pl) return set_err(POD_ERR_INTERNAL, "out of host memory");
+  st = build_prefix_plan(params, num_decode, decode_kv_len, prefix_group, num_groups, prefix_len,
+                         tuning, dev, pl);
+  if (st != POD_OK) {
     delete pl;
-    return POD_OK;
+    return st;
   }
-  if (!out_plan) {
-    delete pl;
-    return set_err(POD_ERR_INVALID_ARGUMENT, "out_plan is NULL");
-  }
-  if (workspace_bytes < pl->ws_bytes) {
-    char buf[128];
-    std::snprintf(buf, sizeof(buf), "workspace has %zu bytes, plan needs %zu", workspace_bytes,
-                  pl->ws_bytes);
-    delete pl;
-    return set_err(POD_ERR_WORKSPACE_TOO_SMALL, buf);
-  }
-  if (!aligned16(workspace)) {
-    delete pl;
-    return set_err(POD_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
-  }
-  pl->ws = (char*)workspace;
-  pl->device = device;
-  hipError_t e = hipMemsetAsync(pl->ws + pl->off_counters, 0, kCounterInts * sizeof(int32_t), stream);
-  if (e != hipSuccess) {
-    delete pl;
-    return hip_err(e, "hipMemsetAsync(counters)");
-  }
-  auto up = [&](const WorkLists& w, const DevLists& d) -> pod_status_t {
-    pod_status_t s2;
-    if ((s2 = upload(pl->ws, d.p_items, w.p_items, stream)) != POD_OK) return s2;
-    if ((s2 = upload(pl->ws, d.d_items, w.d_items, stream)) != POD_OK) return s2;
-    return upload(pl->ws, d.m_tasks, w.m_tasks, stream);
-  };
-  if ((st = up(pl->fused, pl->dl_fused)) != POD_OK ||
-      (!pl->seq_is_fused && (st = up(pl->seq, pl->dl_seq)) != POD_OK) ||
-      (pl->has_bp && (st = up(pl->bp, pl->dl_bp)) != POD_OK)) {
+  return finish_device_plan(pl, device, workspace, workspace_bytes, workspace_needed, stream,
+                            out_plan);
+}
+
+pod_status_t pod_attn_plan_shared_prefix_host(const pod_attn_params_t* params,
+                                              int32_t num_decode, const int32_t* decode_kv_len,
+                                              const int32_t* prefix_group, int32_t num_groups,
+                                              const int32_t* prefix_len,
+                                              const pod_attn_tuning_t* tuning,
+                                              const pod_device_desc_t* device,
+                                              pod_attn_plan_t* out_plan) {
+  if (!out_plan) return set_err(POD_ERR_INVALID_ARGUMENT, "out_plan is NULL");
+  *out_plan = nullptr;
+  if (!device) return set_err(POD_ERR_INVALID_ARGUMENT, "device is NULL");
+  pod_attn_plan_s* pl = new (std::nothrow) pod_attn_plan_s();
+  if (!pl) return set_err(POD_ERR_INTERNAL, "out of host memory");
+  const pod_status_t st = build_prefix_plan(params, num_decode, decode_kv_len, prefix_group,
+                                            num_groups, prefix_len, tuning, *device, pl);
+  if (st != POD_OK) {
     delete pl;
     return st;
   }
@@ -456,7 +575,12 @@ pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t
   hipError_t e;
   if (before_fused && (e = hipEventRecord(before_fused, stream)) != hipSuccess)
     return hip_err(e, "hipEventRecord(before_fused)");
-  if (is_fp8(pl)) {
+  if (pl->has_prefix) {
+    // shared-prefix plan: packed prefix units and suffix units, then the merge
+    if (w.n_groups() > 0 && (e = launch_decode_pack(a, kv_mode_of(pl), w.n_groups(), stream)) !=
+                                hipSuccess)
+      return hip_err(e, "packed decode kernel launch");
+  } else if (is_fp8(pl)) {
     // decode-only FP8 batch: nothing to fuse with; the FP8 decode kernel
     if (w.n_groups() > 0 && (e = launch_decode_fp8(a, kv_mode_of(pl), w.n_groups(), stream)) !=
                                 hipSuccess)
@@ -616,6 +740,7 @@ pod_status_t pod_attn_plan_export(pod_attn_plan_t pl, int32_t which, int32_t* ds
     case 8: v = &pl->bp.p_items; break;
     case 9: v = &pl->bp.m_tasks; break;
     case 10: v = &pl->bp.pool_off; break;
+    case 11: v = &pl->members; break;
     default: return set_err(POD_ERR_INVALID_ARGUMENT, "unknown list id");
   }
   *count = v->size();

@@ -81,6 +81,8 @@ struct KernelArgs {
   float merge_lse_scale;  // factor taking part_lse to log2 (1, or log2(e) for natural log)
   const float* k_scale;   // FP8 KV: per-KV-head scales (device fp32 [Hkv])
   const float* v_scale;
+  const int32_t* d_members;  // shared-prefix plans: decode index of each group member
+  int32_t pack_rpr;          // shared-prefix plans: tile rows per member (min(g, 16))
 };
 
 hipError_t launch_fused(const KernelArgs& a, int kv_mode, int grid, hipStream_t s);
@@ -88,6 +90,7 @@ hipError_t launch_prefill(const KernelArgs& a, int kv_mode, int grid, hipStream_
                           bool batched = false);
 hipError_t launch_decode(const KernelArgs& a, int kv_mode, int grid, hipStream_t s);
 hipError_t launch_decode_fp8(const KernelArgs& a, int kv_mode, int grid, hipStream_t s);
+hipError_t launch_decode_pack(const KernelArgs& a, int kv_mode, int grid, hipStream_t s);
 hipError_t launch_merge(const KernelArgs& a, int grid, hipStream_t s);
 hipError_t launch_probe(int32_t* out, int blocks, hipStream_t s);
 

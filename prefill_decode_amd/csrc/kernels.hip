@@ -589,8 +589,14 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
 // unit's second-to-last step, right after the last V DMA (so the last step's
 // wait for its V covers the ticket too) and returns it in `ticket`; the
 // caller's next claim then costs no round trip of its own.
+//
+// PACKED (queries packed by shared prefix, [PAT] abstract): the tile's rows
+// are the query heads of several decode requests -- row j is head
+// h0 + j % rpr of request members[D_QROW + j / rpr] (rpr = min(g, 16)) -- and
+// every row writes a partial, at D_PART + (j / rpr) Hq D_PSTRIDE + (j % rpr)
+// D_PSTRIDE.
 // ---------------------------------------------------------------------------
-template <int KVM>
+template <int KVM, bool PACKED = false>
 __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* __restrict__ vb0,
                                             char* __restrict__ vb1, int* ahead, int& ticket) {
   const int lane = threadIdx.x & 63;
@@ -613,7 +619,10 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
   u32x4 qf[4];
   {
     const bool ok = j < nq;
-    const uint16_t* qp = a.q_decode + ((int64_t)qi * a.hq + h0 + (ok ? j : 0)) * kHeadDim + 16 * q4;
+    const int jr = ok ? j : 0;
+    const int qrow = PACKED ? ((cptr)a.d_members)[qi + jr / a.pack_rpr] : qi;
+    const int qhead = PACKED ? h0 + jr % a.pack_rpr : h0 + jr;
+    const uint16_t* qp = a.q_decode + ((int64_t)qrow * a.hq + qhead) * kHeadDim + 16 * q4;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
       qf[kk] = ok ? *(const u32x4*)(qp + 64 * (kk >> 1) + 8 * (kk & 1)) : u32x4{0, 0, 0, 0};
@@ -813,7 +822,7 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
   if (j >= nq) return;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse2 = l_tot > 0.0f ? m_run + log2_(l_tot) : kNegInf;
-  if (part < 0) {
+  if (!PACKED && part < 0) {
     uint16_t* op = a.o_decode + ((int64_t)qi * a.hq + h0 + j) * kHeadDim + 4 * q4;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
@@ -823,7 +832,8 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
     }
     if (q4 == 0 && a.lse_decode) a.lse_decode[(int64_t)qi * a.hq + h0 + j] = lse2 * kLn2;
   } else {
-    const int pi = part + j * pstride;
+    const int pi = PACKED ? part + (j / a.pack_rpr) * a.hq * pstride + (j % a.pack_rpr) * pstride
+                          : part + j * pstride;
     float* pp = a.part_o + (int64_t)pi * kHeadDim + 4 * q4;
 #pragma unroll
     for (int db = 0; db < 8; ++db)
@@ -1402,6 +1412,21 @@ __global__ __launch_bounds__(256, 2) void pod_decode_kernel(KernelArgs a) {
   }
 }
 
+// Shared-prefix (packed) decode kernel: one group of four units per
+// workgroup, one unit per wavefront (PAT-style plans).
+template <int KVM>
+__global__ __launch_bounds__(256, 2) void pod_decode_pack_kernel(KernelArgs a) {
+  POD_LDS_OBJECTS
+  (void)s_info;
+  const int wave = rfl(threadIdx.x >> 6);
+  const int d = blockIdx.x * kWavesPerWG + wave;
+  POD_DECODE_BUFFERS(wave)
+  if (d < a.n_d) {
+    int ticket;
+    decode_unit<KVM, true>(a, (cptr)a.d_items + d * D_FIELDS, db0, db1, nullptr, ticket);
+  }
+}
+
 // FP8-cache decode kernel: one group of four units per workgroup, one unit
 // per wavefront (decode-only batches; every run path uses it).
 template <int KVM>
@@ -1635,6 +1660,10 @@ hipError_t launch_prefill(const KernelArgs& a, int kv_mode, int grid, hipStream_
 
 hipError_t launch_decode(const KernelArgs& a, int kv_mode, int grid, hipStream_t s) {
   POD_DISPATCH(pod_decode_kernel, 0)
+}
+
+hipError_t launch_decode_pack(const KernelArgs& a, int kv_mode, int grid, hipStream_t s) {
+  POD_DISPATCH(pod_decode_pack_kernel, 0)
 }
 
 hipError_t launch_decode_fp8(const KernelArgs& a, int kv_mode, int grid, hipStream_t s) {

@@ -318,4 +318,107 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
   *out = std::move(w);
 }
 
+void build_prefix_lists(const Batch& b, const std::vector<int32_t>& group_of,
+                        const std::vector<int32_t>& prefix_len, int64_t decode_wave_slots,
+                        int32_t force_d_splits, WorkLists* out, std::vector<int32_t>* members) {
+  const auto& p = b.params;
+  const int32_t hq = p.num_qo_heads, hkv = p.num_kv_heads, g = hq / hkv;
+  const int32_t nd = (int32_t)b.dkv.size();
+  const int32_t rpr = std::min(g, kDecodeRows);         // rows of one member in a tile
+  const int32_t per_tile = kDecodeRows / rpr;            // members packed per tile
+  const int32_t qchunks = (int32_t)ceil_div(g, kDecodeRows);
+  // groups: the given ones (in order, members in decode order), then every
+  // ungrouped decode as a group of one with no shared prefix
+  struct G { std::vector<int32_t> m; int32_t plen; };
+  std::vector<G> groups(prefix_len.size());
+  for (size_t gi = 0; gi < prefix_len.size(); ++gi) groups[gi].plen = prefix_len[gi];
+  for (int32_t i = 0; i < nd; ++i)
+    if (group_of[i] >= 0) groups[group_of[i]].m.push_back(i);
+  for (int32_t i = 0; i < nd; ++i)
+    if (group_of[i] < 0) groups.push_back(G{{i}, 0});
+  // split length: about two units per decode wavefront, at least kMinDecodeChunk keys
+  double keys = 0.0;
+  for (const G& gr : groups) {
+    if (gr.m.empty()) continue;
+    keys += double(gr.plen) * hkv * qchunks * (double)ceil_div((int64_t)gr.m.size(), per_tile);
+    for (int32_t r : gr.m) keys += double(b.dkv[r] - gr.plen) * hkv * qchunks;
+  }
+  int64_t chunk = kMinDecodeChunk;
+  if (decode_wave_slots > 0 && keys > 0)
+    chunk = std::max<int64_t>(chunk, ceil_div((int64_t)std::ceil(keys / (2.0 * decode_wave_slots)),
+                                              kDecodeStep) * kDecodeStep);
+  constexpr int32_t kMaxSegSplits = kMaxMergeSplits / 2;   // prefix + suffix <= 64
+  auto splits_of = [&](int32_t len) -> std::pair<int32_t, int32_t> {   // (count, keys per split)
+    if (len <= 0) return {0, 0};
+    const int32_t steps = (int32_t)ceil_div(len, kDecodeStep);
+    int64_t s = force_d_splits > 0 ? force_d_splits : ceil_div(len, chunk);
+    s = std::max<int64_t>(1, std::min<int64_t>({s, (int64_t)kMaxSegSplits, (int64_t)steps}));
+    const int32_t per = (int32_t)ceil_div(steps, s) * kDecodeStep;
+    return {(int32_t)ceil_div(len, per), per};
+  };
+  WorkLists w;
+  members->clear();
+  int32_t n_partials = 0;
+  struct DI { std::array<int32_t, D_FIELDS> f; int32_t work; };
+  std::vector<DI> items;
+  for (const G& gr : groups) {
+    if (gr.m.empty()) continue;
+    const int32_t moff = (int32_t)members->size();
+    members->insert(members->end(), gr.m.begin(), gr.m.end());
+    const auto [sp, pp] = splits_of(gr.plen);
+    int32_t ss_max = 0;
+    for (int32_t r : gr.m) ss_max = std::max(ss_max, splits_of(b.dkv[r] - gr.plen).first);
+    const int32_t smax = sp + ss_max;
+    const int32_t gbase = n_partials;
+    n_partials += (int32_t)gr.m.size() * hq * smax;
+    auto region = [&](int32_t rl, int32_t h) { return gbase + (rl * hq + h) * smax; };
+    const int32_t nm = (int32_t)gr.m.size();
+    for (int32_t kh = 0; kh < hkv; ++kh)
+      for (int32_t qc = 0; qc < qchunks; ++qc) {
+        const int32_t h0 = kh * g + qc * kDecodeRows;
+        const int32_t nh = std::min(kDecodeRows, g - qc * kDecodeRows);
+        // prefix: packs of per_tile members
+        for (int32_t m0 = 0; m0 < nm && gr.plen > 0; m0 += per_tile) {
+          const int32_t cnt = std::min(per_tile, nm - m0);
+          for (int32_t k = 0; k < sp; ++k) {
+            const int32_t kb = k * pp, ke = std::min(gr.plen, (k + 1) * pp);
+            DI it;
+            it.f = {moff + m0, h0, (cnt - 1) * rpr + nh, kb, ke, (int32_t)b.qo.size() + gr.m[0],
+                    region(m0, h0) + k, smax};
+            it.work = ke - kb;
+            items.push_back(it);
+          }
+        }
+        // suffixes
+        for (int32_t rl = 0; rl < nm; ++rl) {
+          const int32_t r = gr.m[rl];
+          const auto [ss, ps] = splits_of(b.dkv[r] - gr.plen);
+          for (int32_t k = 0; k < ss; ++k) {
+            const int32_t kb = gr.plen + k * ps, ke = std::min(b.dkv[r], gr.plen + (k + 1) * ps);
+            DI it;
+            it.f = {moff + rl, h0, nh, kb, ke, (int32_t)b.qo.size() + r,
+                    region(rl, h0) + sp + k, smax};
+            it.work = ke - kb;
+            items.push_back(it);
+          }
+        }
+      }
+    for (int32_t rl = 0; rl < nm; ++rl) {
+      const int32_t n = sp + splits_of(b.dkv[gr.m[rl]] - gr.plen).first;
+      for (int32_t h = 0; h < hq; ++h) {
+        w.m_tasks.push_back(gr.m[rl] * hq + h);
+        w.m_tasks.push_back(region(rl, h));
+        w.m_tasks.push_back(1);
+        w.m_tasks.push_back(n | (1 << 16));
+      }
+    }
+    w.d_splits_max = std::max(w.d_splits_max, smax);
+  }
+  std::stable_sort(items.begin(), items.end(), [](const DI& a, const DI& c) { return a.work > c.work; });
+  for (auto& it : items) w.d_items.insert(w.d_items.end(), it.f.begin(), it.f.end());
+  w.pool_off.assign(2, 0);
+  w.n_partials = n_partials;
+  *out = std::move(w);
+}
+
 }  // namespace pod

@@ -157,4 +157,22 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev,
                  int32_t d_units_per_slot, int32_t force_p_splits, int32_t force_d_splits,
                  WorkLists* out, bool decodes_as_prefill = false);
 
+// PAT-style lists for decode requests that share KV prefixes ([PAT]
+// abstract: pack queries by shared prefix, forward with KV splitting, merge
+// by online softmax).  group_of[i] in [0, prefix_len.size()) or -1; a group's
+// members share their first prefix_len[g] tokens (whole pages).
+//   Prefix units: for each KV head (and block of 16 query heads), up to
+//     16 / min(g, 16) members of a group packed into one 16-row decode tile
+//     over keys of the prefix, read through the first member's page table.
+//   Suffix units: each member's own keys [P, kv).
+// Every (member, query head) owns a region of smax partial slots (prefix
+// splits first, then its suffix splits); a unit's row j writes slot
+//   D_PART + (j / rpr) * Hq * D_PSTRIDE + (j % rpr) * D_PSTRIDE,
+// rpr = min(g, 16), D_PSTRIDE = smax, and D_QROW is the offset of its first
+// member in `members` (the decode index of row j is members[D_QROW + j / rpr]).
+// One merge task per (decode, query head) combines its region.
+void build_prefix_lists(const Batch& b, const std::vector<int32_t>& group_of,
+                        const std::vector<int32_t>& prefix_len, int64_t decode_wave_slots,
+                        int32_t force_d_splits, WorkLists* out, std::vector<int32_t>* members);
+
 }  // namespace pod

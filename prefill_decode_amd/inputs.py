@@ -20,6 +20,11 @@ Llama-3-8B-shaped layers).  No dataset is involved; every value is synthetic:
 * ``batched``   32/8; 4 chunks {128, 256, 512, 640} at kv ~ U[2048, 8192];
                 192 decodes at kv ~ U[512, 16384]; paged.  ``n_dec`` sweeps
                 {32, 64, 128, 256}.
+* ``l70b_prefix`` 64/8, decode-only with shared prefixes (the workload class
+                of [PAT]'s abstract: system prompts, templates, RAG shared
+                across requests): 128 decodes in 16 groups of 8, each group
+                sharing a 2048-token prefix (the same pages), each request
+                with its own ~ U[64, 1024] tokens after it; paged.
 
 Conventions: request order is all prefill requests, then all decodes;
 ``uniform in [a, b]`` is integers with both ends included; Q/K/V values are
@@ -68,6 +73,10 @@ class BatchSpec:
     random_pages: bool = True
     extra_pages: int = 3             # unreferenced pool pages (poisoned)
     kv_dtype: str = "bf16"           # "bf16" | "fp8_e4m3"
+    # decode requests sharing a KV prefix: ((decode ids, prefix tokens), ..);
+    # the members' first prefix tokens are the same pages (prefix tokens are
+    # a multiple of page_size)
+    prefix_groups: Tuple = ()
 
     @property
     def num_prefill(self) -> int:
@@ -119,6 +128,13 @@ def config_spec(name: str, n_dec: Optional[int] = None) -> BatchSpec:
         return BatchSpec(name if n_dec is None else f"batched_d{nd}", 32, 8,
                          (128, 256, 512, 640), tuple(int(x) for x in pkv),
                          tuple(int(x) for x in dec), seed=seed)
+    if name == "l70b_prefix":
+        seed = 1239
+        rng = np.random.default_rng([seed, _TAG_LEN])
+        own = rng.integers(64, 1024, size=128, endpoint=True)
+        groups = tuple((tuple(range(8 * g, 8 * g + 8)), 2048) for g in range(16))
+        return BatchSpec(name, 64, 8, (), (), tuple(2048 + int(x) for x in own), seed=seed,
+                         prefix_groups=groups)
     raise ValueError(f"unknown config {name!r}")
 
 
@@ -217,16 +233,53 @@ def page_table(spec: BatchSpec):
 
     Pages are handed out in request order from a seeded permutation of the
     pool (or in order when ``random_pages`` is False); ``extra_pages``
-    pool pages are referenced by no request."""
+    pool pages are referenced by no request.  A decode request of a prefix
+    group starts with the group's shared prefix pages (handed out once, at the
+    group's first member) and continues with pages of its own."""
+    n_p = spec.num_prefill
+    ps = spec.page_size
+    shared_of = {}                      # decode id -> (group, prefix pages)
+    for gi, (members, plen) in enumerate(spec.prefix_groups):
+        if plen % ps or plen < 1:
+            raise ValueError("a shared prefix is a positive whole number of pages")
+        for m in members:
+            if spec.decode_kv_len[m] < plen:
+                raise ValueError("a member is shorter than its group's prefix")
+            shared_of[int(m)] = (gi, plen // ps)
     npg = [spec.num_pages_of(L) for L in spec.kv_lens]
-    indptr = np.zeros(len(npg) + 1, dtype=np.int32)
-    indptr[1:] = np.cumsum(npg)
-    pool = int(indptr[-1]) + spec.extra_pages
+    own = list(npg)
+    groups_seen = set()
+    for m, (gi, pp) in shared_of.items():
+        own[n_p + m] -= pp
+        if gi not in groups_seen:
+            groups_seen.add(gi)
+            own[n_p + m] += pp           # the first member seen allocates them
+    total = int(sum(own))
+    pool = total + spec.extra_pages
     if spec.random_pages:
         perm = np.random.default_rng([spec.seed, _TAG_PAGES]).permutation(pool)
     else:
         perm = np.arange(pool)
-    return indptr, perm[: int(indptr[-1])].astype(np.int32), pool
+    indptr = np.zeros(len(npg) + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum(npg)
+    indices = np.empty(int(indptr[-1]), dtype=np.int32)
+    nxt = 0
+    group_pages = {}
+    for r, n in enumerate(npg):
+        out = indices[indptr[r]:indptr[r + 1]]
+        sh = shared_of.get(r - n_p) if r >= n_p else None
+        k = 0
+        if sh is not None:
+            gi, pp = sh
+            if gi not in group_pages:
+                group_pages[gi] = perm[nxt:nxt + pp].astype(np.int32)
+                nxt += pp
+            out[:pp] = group_pages[gi]
+            k = pp
+        out[k:] = perm[nxt:nxt + (n - k)]
+        nxt += n - k
+    assert nxt == total
+    return indptr, indices, pool
 
 
 def _base_dict(spec: BatchSpec) -> Dict:
@@ -240,6 +293,7 @@ def _base_dict(spec: BatchSpec) -> Dict:
         "causal": spec.causal,
         "sm_scale": spec.sm_scale,
         "kv_dtype": spec.kv_dtype,
+        "prefix_groups": spec.prefix_groups,
         "prefill_qo_len": np.array(spec.prefill_qo_len, dtype=np.int32),
         "prefill_kv_len": np.array(spec.prefill_kv_len, dtype=np.int32),
         "decode_kv_len": np.array(spec.decode_kv_len, dtype=np.int32),

@@ -10,6 +10,8 @@ indices as int32, and only the visible (query, key) pairs:
 Re-reads of K/V by several prefill tiles, split partials, masked MFMA work on
 diagonal tiles and the padding of decode rows to 16 are overheads, not counted.
 An FP8 KV cache counts one byte per K or V element plus its per-head scales.
+A batch with shared prefixes counts each group's prefix K/V once (the pages
+are shared; [PAT] abstract); ``bytes_unshared`` counts it once per member.
 """
 
 import numpy as np
@@ -42,14 +44,21 @@ def algorithmic_counts(b) -> dict:
         kv_b = kv_tokens * hkv * d * kv_elem * 2              # K + V
         return qo_b + kv_b + (pages * 4 if paged else 0.0)
 
+    try:
+        groups = get("prefix_groups") or ()
+    except (AttributeError, KeyError):
+        groups = ()
+    shared = float(sum((len(m) - 1) * pl for m, pl in groups))   # tokens read once, not per member
     bp = part_bytes(rows_p, float(np.sum(pkv)), float(np.sum(np.ceil(pkv / ps))))
-    bd = part_bytes(rows_d, float(np.sum(dkv)), float(np.sum(np.ceil(dkv / ps))))
+    bd_unshared = part_bytes(rows_d, float(np.sum(dkv)), float(np.sum(np.ceil(dkv / ps))))
+    bd = bd_unshared - shared * hkv * d * kv_elem * 2
     if kv_elem == 1.0:
         bd += 2 * hkv * 4                                     # K and V scales
+        bd_unshared += 2 * hkv * 4
     fp = 4.0 * d * hq * pairs_p
     fd = 4.0 * d * hq * pairs_d
     return {"flops": fp + fd, "bytes": bp + bd, "flops_prefill": fp, "flops_decode": fd,
-            "bytes_prefill": bp, "bytes_decode": bd}
+            "bytes_prefill": bp, "bytes_decode": bd, "bytes_unshared": bp + bd_unshared}
 
 
 def overlap_roofline_s(c: dict) -> float:
