@@ -272,9 +272,13 @@ pod_status_t pod_attn_plan_host(const pod_attn_params_t* params,
  *                  member's kv_len.  The members' page tables must hold the
  *                  same pages for these tokens (the kernel reads the prefix
  *                  through the group's first member's table).
- * For each KV head, the rows of up to 16 / min(Hq/Hkv, 16) members are packed
- * into one 16-row decode tile over the prefix; each member's own keys run as
- * ordinary units; every (request, head) result is merged by log-sum-exp.
+ * For each KV head, the rows of up to 64 / min(Hq/Hkv, 16) members are packed
+ * into one workgroup tile over the prefix (four 16-row MFMA tiles sharing
+ * every K/V step through LDS, so the prefix is read once per tile); each
+ * member's own keys run as ordinary decode units; every (request, head)
+ * result is merged by log-sum-exp.  pod_attn_plan_export lists the prefix
+ * tiles as list 0 (in decode-item fields, up to 64 rows) and the suffix
+ * units as list 1.
  * pod_attn_run runs this packed path; pod_attn_sequential_run and
  * pod_attn_streams_run run the ordinary (unshared) decode of the same batch,
  * the baseline.  Workspace, ownership and errors as pod_attn_plan, plus

@@ -577,8 +577,8 @@ pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t
     return hip_err(e, "hipEventRecord(before_fused)");
   if (pl->has_prefix) {
     // shared-prefix plan: packed prefix units and suffix units, then the merge
-    if (w.n_groups() > 0 && (e = launch_decode_pack(a, kv_mode_of(pl), w.n_groups(), stream)) !=
-                                hipSuccess)
+    const int pgrid = w.n_p() + w.n_groups();
+    if (pgrid > 0 && (e = launch_decode_pack(a, kv_mode_of(pl), pgrid, stream)) != hipSuccess)
       return hip_err(e, "packed decode kernel launch");
   } else if (is_fp8(pl)) {
     // decode-only FP8 batch: nothing to fuse with; the FP8 decode kernel

@@ -844,6 +844,198 @@ __device__ __forceinline__ void decode_unit(const KernelArgs& a, cptr it, char* 
 }
 
 // ---------------------------------------------------------------------------
+// Shared-prefix tile ([PAT] abstract: queries packed by shared prefix so that
+// the prefix's KV is loaded once, in a tile sized to the pack): a workgroup
+// takes up to 64 rows -- row jr is query head h0 + jr % rpr of decode request
+// members[D_QROW + jr / rpr], rpr = min(g, 16) -- over keys [kb, ke) of one
+// KV head, read through request D_KVREQ's page table.  Wave w owns rows
+// 16w .. 16w + 15 as one 16-row MFMA tile (the decode unit's step, with K
+// read from LDS instead of registers); the four waves share every 32-key K/V
+// step, which they stage together by LDS DMA (wave w: keys 8w .. 8w + 7 of
+// the step) into double buffers, so each key's bytes leave HBM once per
+// workgroup instead of once per 16 rows.  Every row writes a partial, at
+// D_PART + (jr / rpr) Hq D_PSTRIDE + (jr % rpr) D_PSTRIDE.
+//
+// LDS: step buffers of parity 0 in X, of parity 1 in Y (K at +0, V at +8
+// KiB).  K rows keep 16-byte chunk c at position c ^ (row & 15), so the
+// sixteen keys of an MFMA operand read fall in sixteen distinct bank groups;
+// V rows use the decode unit's layout.
+// ---------------------------------------------------------------------------
+template <int KVM>
+__device__ __forceinline__ void prefix_tile(const KernelArgs& a, cptr it, char* __restrict__ bx,
+                                            char* __restrict__ by) {
+  const int lane = threadIdx.x & 63;
+  const int wave = rfl(threadIdx.x >> 6);
+  const int j = lane & 15, q4 = lane >> 4;
+  const int qi = it[D_QROW], h0 = it[D_HEAD0], nq = it[D_NQ];
+  const int kb = it[D_KV_BEGIN], ke = it[D_KV_END], kvreq = it[D_KVREQ];
+  const int part = it[D_PART], pstride = it[D_PSTRIDE];
+  const int rpr = a.pack_rpr;
+  const int kvh = h0 / a.group;
+  const uint32_t tok = (uint32_t)a.hkv * kRowBytes;
+  const char* kbase = (const char*)a.k + kvh * kRowBytes;
+  const char* vbase = (const char*)a.v + kvh * kRowBytes;
+  KvAddr<KVM> addr;
+  addr.init(a, kvreq);
+  const int span = ke - kb;
+  const int nsteps = (span + kDecodeStep - 1) / kDecodeStep;
+  const int nfull = span / kDecodeStep;
+  const int jr = 16 * wave + j;                      // tile row of this lane's query
+  const bool active = 16 * wave < nq;                // wave-uniform
+
+  // Q operand kk: lane holds query jr, d = 32 kk + 8 q4 .. + 7
+  u32x4 qf[4];
+  {
+    const bool ok = jr < nq;
+    const int jq = ok ? jr : 0;
+    const int qrow = ((cptr)a.d_members)[qi + jq / rpr];
+    const uint16_t* qp = a.q_decode + ((int64_t)qrow * a.hq + h0 + jq % rpr) * kHeadDim + 8 * q4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qf[kk] = ok ? *(const u32x4*)(qp + 32 * kk) : u32x4{0, 0, 0, 0};
+  }
+
+  // staging of step s: wave w deposits keys 8w + 4i + L/16 (i = 0, 1) of the
+  // step, chunk position L%16, into the K and V halves of `buf`; the keys
+  // lie in one 16-key block (page_size >= 16) whose rows are clamped to the
+  // last key (finite data, never read past it)
+  const int lastb = (ke - 1) & ~15;
+  const int dq = lane >> 4, dc = lane & 15;
+  auto stage = [&](int s, char* buf) {
+    char* kd = buf + 8 * wave * kRowBytes;
+    char* vd = buf + kDecStepBytes + 8 * wave * kRowBytes;
+    if (KVM != KV_PAGED_NARROW) {
+      const int bs = min(kb + s * kDecodeStep + 16 * (wave >> 1), lastb);
+      const int64_t rw = addr.block_row(bs);
+      const __amdgpu_buffer_rsrc_t rk = rsrc(kbase + rw * tok), rv = rsrc(vbase + rw * tok);
+      const int rmax = ke - 1 - bs;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 8 * (wave & 1) + 4 * i + dq;       // row in the 16-key block
+        const int rs = 8 * wave + 4 * i + dq;             // row in the step
+        const uint32_t ro = (uint32_t)min(r, rmax) * tok;
+        dma16<kStream>(rk, kd + 4 * i * kRowBytes, ro + 16u * (dc ^ kswz(rs)), 0);
+        dma16<kStream>(rv, vd + 4 * i * kRowBytes, ro + 16u * (dc ^ vswz(rs)), 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int rs = 8 * wave + 4 * i + dq;
+        const int64_t rw = addr.row(min(kb + s * kDecodeStep + rs, ke - 1));
+        *(u32x4*)(kd + 4 * i * kRowBytes + 16 * lane) =
+            gload(kbase + rw * tok + 16 * (dc ^ kswz(rs)));
+        *(u32x4*)(vd + 4 * i * kRowBytes + 16 * lane) =
+            gload(vbase + rw * tok + 16 * (dc ^ vswz(rs)));
+      }
+    }
+  };
+
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = kNegInf, l_run = 0.0f;
+  const float sl2 = a.scale_log2;
+  // K operand reads: key 16 sb + j, chunk 4 kk + q4 at position (4 kk + q4) ^ j
+  // V^T read lanes: rows 4*q4 + j/4 (+16), chunk 2 db + (j&3)/2, half j&1
+  const int vrow0 = 4 * q4 + (j >> 2);
+  const int vsw = vswz(vrow0);
+
+  auto step = [&](int s, const char* buf) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int k0 = kb + s * kDecodeStep;
+    f32x4 s0 = {}, s1 = {};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const char* kp = buf + j * kRowBytes + 16 * ((4 * kk + q4) ^ j);
+      const u32x4 ka = *(const u32x4*)kp;
+      const u32x4 kc = *(const u32x4*)(kp + 16 * kRowBytes);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(ka), as_bf(qf[kk]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(kc), as_bf(qf[kk]), s1, 0, 0, 0);
+    }
+    // s0[r]: key k0 + 4*q4 + r; s1[r]: key k0 + 16 + 4*q4 + r; query jr
+    float x[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = s0[r];
+      x[4 + r] = s1[r];
+    }
+    if (s >= nfull) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (k0 + 4 * q4 + r >= ke) x[r] = kNegInf;
+        if (k0 + 16 + 4 * q4 + r >= ke) x[4 + r] = kNegInf;
+      }
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) mx = fmax_(mx, x[r]);
+    mx = max_x32(max_x16(mx));
+    const float m_new = fmax_(m_run, mx * sl2);
+    if (any_lane(m_new > m_run)) {
+      const float alpha = exp2_(m_run - (m_new == kNegInf ? 0.0f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float nm = m_run == kNegInf ? 0.0f : -m_run;
+    float ls = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      x[r] = exp2_(__builtin_fmaf(x[r], sl2, nm));
+      ls += x[r];
+    }
+    l_run += ls;
+    const u32x4 pb = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                      pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+    const char* vt = buf + kDecStepBytes + vrow0 * kRowBytes + 8 * (j & 1);
+    u32x4 af[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const char* cp = vt + 16 * ((2 * db + ((j & 3) >> 1)) ^ vsw);
+      const u32x2 lo = tr_read(cp);
+      const u32x2 hi = tr_read(cp + 16 * kRowBytes);
+      af[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(af[db]), as_bf(pb), o[db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // step s reads the buffers of parity s & 1 (X or Y) while the DMAs of step
+  // s + 1 fill the other object; the barrier at the top of a step makes the
+  // whole step visible and frees the buffers the DMAs are about to refill
+  stage(0, bx);
+  for (int s = 0; s < nsteps; s += 2) {
+    wait_vmem<0>();
+    __syncthreads();
+    if (s + 1 < nsteps) stage(s + 1, by);
+    if (active) step(s, bx);
+    if (s + 1 < nsteps) {
+      wait_vmem<0>();
+      __syncthreads();
+      if (s + 2 < nsteps) stage(s + 2, bx);
+      if (active) step(s + 1, by);
+    }
+  }
+  // the buffers are reused by the workgroup's next unit
+  __syncthreads();
+
+  const float l_tot = sum_x32(sum_x16(l_run));
+  if (jr >= nq) return;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse2 = l_tot > 0.0f ? m_run + log2_(l_tot) : kNegInf;
+  const int pi = part + (jr / rpr) * a.hq * pstride + (jr % rpr) * pstride;
+  float* pp = a.part_o + (int64_t)pi * kHeadDim + 4 * q4;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    *(f32x4*)(pp + 16 * db) = f32x4{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv,
+                                    o[db][3] * inv};
+  if (q4 == 0) a.part_lse[pi] = lse2;
+}
+
+// ---------------------------------------------------------------------------
 // Decode over an FP8 E4M3 KV cache with one scale per KV head for K and for
 // V ("Prefill vs. Decode GPU Utilization Imbalance", section "Quantization
 // and compression as a lever on both the bandwidth and capacity problem"):
@@ -1412,14 +1604,19 @@ __global__ __launch_bounds__(256, 2) void pod_decode_kernel(KernelArgs a) {
   }
 }
 
-// Shared-prefix (packed) decode kernel: one group of four units per
-// workgroup, one unit per wavefront (PAT-style plans).
+// Shared-prefix (packed) decode kernel: workgroups below n_p take one
+// prefix tile each (the plan's p_items, in decode-item fields), the rest one
+// group of four suffix units, one per wavefront (PAT-style plans).
 template <int KVM>
 __global__ __launch_bounds__(256, 2) void pod_decode_pack_kernel(KernelArgs a) {
   POD_LDS_OBJECTS
   (void)s_info;
   const int wave = rfl(threadIdx.x >> 6);
-  const int d = blockIdx.x * kWavesPerWG + wave;
+  if ((int)blockIdx.x < a.n_p) {
+    prefix_tile<KVM>(a, (cptr)a.p_items + blockIdx.x * D_FIELDS, ldsx, ldsy);
+    return;
+  }
+  const int d = ((int)blockIdx.x - a.n_p) * kWavesPerWG + wave;
   POD_DECODE_BUFFERS(wave)
   if (d < a.n_d) {
     int ticket;

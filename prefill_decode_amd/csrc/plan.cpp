@@ -324,9 +324,12 @@ void build_prefix_lists(const Batch& b, const std::vector<int32_t>& group_of,
   const auto& p = b.params;
   const int32_t hq = p.num_qo_heads, hkv = p.num_kv_heads, g = hq / hkv;
   const int32_t nd = (int32_t)b.dkv.size();
-  const int32_t rpr = std::min(g, kDecodeRows);         // rows of one member in a tile
-  const int32_t per_tile = kDecodeRows / rpr;            // members packed per tile
+  const int32_t rpr = std::min(g, kDecodeRows);         // tile rows of one member
   const int32_t qchunks = (int32_t)ceil_div(g, kDecodeRows);
+  // members per prefix tile in a query-head chunk of nh heads: a partial
+  // chunk (g > 16, not a multiple of 16) holds one member, so that row jr is
+  // always head h0 + jr % rpr of member jr / rpr
+  auto per_tile = [&](int32_t nh) { return nh == rpr ? kPrefixTileRows / rpr : 1; };
   // groups: the given ones (in order, members in decode order), then every
   // ungrouped decode as a group of one with no shared prefix
   struct G { std::vector<int32_t> m; int32_t plen; };
@@ -336,11 +339,17 @@ void build_prefix_lists(const Batch& b, const std::vector<int32_t>& group_of,
     if (group_of[i] >= 0) groups[group_of[i]].m.push_back(i);
   for (int32_t i = 0; i < nd; ++i)
     if (group_of[i] < 0) groups.push_back(G{{i}, 0});
-  // split length: about two units per decode wavefront, at least kMinDecodeChunk keys
+  // split length: about two units per decode wavefront, at least
+  // kMinDecodeChunk keys; a prefix tile holds all four wavefronts of its
+  // workgroup for its keys
   double keys = 0.0;
   for (const G& gr : groups) {
     if (gr.m.empty()) continue;
-    keys += double(gr.plen) * hkv * qchunks * (double)ceil_div((int64_t)gr.m.size(), per_tile);
+    for (int32_t qc = 0; qc < qchunks; ++qc) {
+      const int32_t nh = std::min(kDecodeRows, g - qc * kDecodeRows);
+      keys += double(gr.plen) * hkv * kWavesPerWG *
+              (double)ceil_div((int64_t)gr.m.size(), per_tile(nh));
+    }
     for (int32_t r : gr.m) keys += double(b.dkv[r] - gr.plen) * hkv * qchunks;
   }
   int64_t chunk = kMinDecodeChunk;
@@ -360,7 +369,7 @@ void build_prefix_lists(const Batch& b, const std::vector<int32_t>& group_of,
   members->clear();
   int32_t n_partials = 0;
   struct DI { std::array<int32_t, D_FIELDS> f; int32_t work; };
-  std::vector<DI> items;
+  std::vector<DI> tiles, items;
   for (const G& gr : groups) {
     if (gr.m.empty()) continue;
     const int32_t moff = (int32_t)members->size();
@@ -377,16 +386,17 @@ void build_prefix_lists(const Batch& b, const std::vector<int32_t>& group_of,
       for (int32_t qc = 0; qc < qchunks; ++qc) {
         const int32_t h0 = kh * g + qc * kDecodeRows;
         const int32_t nh = std::min(kDecodeRows, g - qc * kDecodeRows);
-        // prefix: packs of per_tile members
-        for (int32_t m0 = 0; m0 < nm && gr.plen > 0; m0 += per_tile) {
-          const int32_t cnt = std::min(per_tile, nm - m0);
+        const int32_t pt = per_tile(nh);
+        // prefix: tiles of up to pt members
+        for (int32_t m0 = 0; m0 < nm && gr.plen > 0; m0 += pt) {
+          const int32_t cnt = std::min(pt, nm - m0);
           for (int32_t k = 0; k < sp; ++k) {
             const int32_t kb = k * pp, ke = std::min(gr.plen, (k + 1) * pp);
             DI it;
             it.f = {moff + m0, h0, (cnt - 1) * rpr + nh, kb, ke, (int32_t)b.qo.size() + gr.m[0],
                     region(m0, h0) + k, smax};
             it.work = ke - kb;
-            items.push_back(it);
+            tiles.push_back(it);
           }
         }
         // suffixes
@@ -414,9 +424,12 @@ void build_prefix_lists(const Batch& b, const std::vector<int32_t>& group_of,
     }
     w.d_splits_max = std::max(w.d_splits_max, smax);
   }
-  std::stable_sort(items.begin(), items.end(), [](const DI& a, const DI& c) { return a.work > c.work; });
+  auto longest_first = [](const DI& a, const DI& c) { return a.work > c.work; };
+  std::stable_sort(tiles.begin(), tiles.end(), longest_first);
+  std::stable_sort(items.begin(), items.end(), longest_first);
+  for (auto& it : tiles) w.p_items.insert(w.p_items.end(), it.f.begin(), it.f.end());
   for (auto& it : items) w.d_items.insert(w.d_items.end(), it.f.begin(), it.f.end());
-  w.pool_off.assign(2, 0);
+  w.pool_off = {0, w.n_p()};
   w.n_partials = n_partials;
   *out = std::move(w);
 }

@@ -24,6 +24,7 @@ constexpr int kWaveRows = 64;       // rows per wave: two 32-row MFMA blocks
 constexpr int kPrefillKeys = 64;    // keys per prefill KV tile
 constexpr int kDecodeStep = 32;     // keys per decode step (2 MFMA key blocks)
 constexpr int kDecodeRows = 16;     // decode query tile (MFMA 16 rows)
+constexpr int kPrefixTileRows = 64; // shared-prefix tile: 4 waves x 16 rows
 constexpr int kWavesPerWG = 4;
 constexpr int kMaxXcds = 16;
 constexpr int kMaxPrefillSplits = 16;
@@ -161,10 +162,12 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev,
 // abstract: pack queries by shared prefix, forward with KV splitting, merge
 // by online softmax).  group_of[i] in [0, prefix_len.size()) or -1; a group's
 // members share their first prefix_len[g] tokens (whole pages).
-//   Prefix units: for each KV head (and block of 16 query heads), up to
-//     16 / min(g, 16) members of a group packed into one 16-row decode tile
-//     over keys of the prefix, read through the first member's page table.
-//   Suffix units: each member's own keys [P, kv).
+//   Prefix tiles (out->p_items, decode-item fields): for each KV head (and
+//     block of 16 query heads), up to 64 / min(g, 16) members of a group
+//     packed into one workgroup tile of <= 64 rows over keys of the prefix,
+//     read through the first member's page table (one member per tile in a
+//     partial block of heads, g > 16 not a multiple of 16).
+//   Suffix units (out->d_items): each member's own keys [P, kv).
 // Every (member, query head) owns a region of smax partial slots (prefix
 // splits first, then its suffix splits); a unit's row j writes slot
 //   D_PART + (j / rpr) * Hq * D_PSTRIDE + (j % rpr) * D_PSTRIDE,

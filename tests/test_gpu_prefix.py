@@ -2,8 +2,9 @@
 oracle ([PAT] abstract: queries packed by shared prefix, KV splits, a final
 online-softmax merge).
 
-Cases: group sizes 1 to 17, 1 to 32 query heads per KV head (packs of 16,
-8, 4, 2 and 1 members per tile, and the ragged pack of g = 6), prefixes
+Cases: group sizes 1 to 20, 1 to 32 query heads per KV head (workgroup
+tiles of 64, 16, 8, 4 and 2 members, the ragged pack of g = 6 and the
+partial head block of g = 24), prefixes
 that are the whole sequence, ungrouped requests beside groups, pages of 8,
 16 and 64 tokens, forced KV splits, a sharp softmax, NaN in every cache slot
 no token owns.  The packed path (pod_attn_run) and the unshared baseline of
@@ -44,6 +45,10 @@ def prefix_specs():
         _spec("p_single", 16, 2, [48, 400], [((0,), 48), ((1,), 384)], seed=708),
         _spec("p_page8", 16, 4, [40 + x for x in own(5, 0, 90)], [((0, 1, 2, 3, 4), 40)],
               seed=709, page_size=8),
+        _spec("p_g24", 48, 2, [96 + x for x in own(6, 0, 200)], [(tuple(range(6)), 96)],
+              seed=711),
+        _spec("p_g8_40", 32, 4, [160 + x for x in own(40, 0, 400)],
+              [(tuple(range(0, 40, 2)), 160), (tuple(range(1, 40, 2)), 128)], seed=712),
         _spec("p_page64", 32, 8, [640 + x for x in own(6, 1, 500)], [((0, 2, 4), 640),
                                                                       ((1, 3), 576)],
               seed=710, page_size=64),

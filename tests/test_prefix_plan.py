@@ -54,19 +54,20 @@ def _units(spec, pl):
     """Per (request, head): list of (kb, ke, kvreq, slot) from the packed lists."""
     hq, hkv = spec.num_qo_heads, spec.num_kv_heads
     rpr = min(hq // hkv, 16)
-    D = pl.export(1).reshape(-1, D_F)
+    T = pl.export(0).reshape(-1, D_F)          # prefix tiles (<= 64 rows)
+    D = pl.export(1).reshape(-1, D_F)          # suffix units (<= 16 rows)
     mem = pl.export(11)
     per = {}
-    for it in D:
+    for it, cap in [(t, 64) for t in T] + [(d, 16) for d in D]:
         q0, h0, nq, kb, ke, kvreq, part, ps = (int(x) for x in it)
-        assert 1 <= nq <= 16 and 0 <= kb < ke
+        assert 1 <= nq <= cap and 0 <= kb < ke
         for j in range(nq):
             r = int(mem[q0 + j // rpr])
             h = h0 + j % rpr
             assert h // (hq // hkv) == h0 // (hq // hkv)        # one KV head per unit
             slot = part + (j // rpr) * hq * ps + (j % rpr) * ps
             per.setdefault((r, h), []).append((kb, ke, kvreq, slot))
-    return per, D, mem
+    return per, np.concatenate([T, D]), mem
 
 
 CASES = [
@@ -77,6 +78,8 @@ CASES = [
     ("g1_mha", 8, 8, [48, 49, 50, 200], [((0, 1, 2), 48)]),
     ("g16", 32, 2, [300, 301, 40], [((0, 1), 288)]),
     ("g32_two_chunks", 64, 2, [70, 90], [((0, 1), 64)]),
+    ("g24_partial_chunk", 48, 2, [64, 70, 80, 96, 65], [((0, 1, 2, 3, 4), 64)]),
+    ("g8_big_group", 32, 4, [100 + i for i in range(20)], [(tuple(range(20)), 96)]),
     ("g6_ragged_pack", 12, 2, [64, 65, 66, 67, 68], [((0, 1, 2, 3, 4), 64)]),
     ("prefix_is_all", 16, 2, [64, 64, 64], [((0, 1, 2), 64)]),
     ("ungrouped_only", 16, 2, [64, 65], []),
@@ -127,17 +130,23 @@ def test_prefix_lists_cover_keys_once(case, splits):
 
 
 def test_prefix_units_are_shared_by_the_pack():
-    # g = 4: rpr 4, four members per 16-row tile; a group of 9 members over a
-    # 160-token prefix packs into ceil(9/4) = 3 tiles per KV head and split
+    # g = 4: rpr 4, sixteen members per 64-row workgroup tile; a group of 9
+    # members over a 160-token prefix is one tile (36 rows) per KV head and
+    # split, so each prefix key is read once per KV head, not once per member
     spec = _spec("pack", 16, 4, [200] * 9 + [150], [(tuple(range(9)), 160)])
     pl = _host_plan(spec, decode_kv_splits=2)
+    T = pl.export(0).reshape(-1, D_F)
+    assert len(T) == 4 * 2
+    assert all(int(x) == 36 for x in T[:, 2])
+    assert int((T[:, 4] - T[:, 3]).sum()) == 4 * 160
     D = pl.export(1).reshape(-1, D_F)
-    prefix_units = D[(D[:, 5] == 0) & (D[:, 4] <= 160)]
-    assert len(prefix_units) == 4 * 3 * 2
-    assert sorted(int(x) for x in prefix_units[:, 2]) == [4] * 8 + [16] * 16
-    # keys read for the prefix: 3 packs per KV head, not 9 requests
-    prefix_keys = int((prefix_units[:, 4] - prefix_units[:, 3]).sum())
-    assert prefix_keys == 4 * 3 * 160
+    assert np.all(D[:, 2] <= 4) and not np.any((D[:, 5] < 9) & (D[:, 3] < 160))
+    # g = 24 (a partial block of 8 heads per KV head): full blocks pack four
+    # members, the partial block one member per tile
+    spec = _spec("g24", 48, 2, [64] * 5, [(tuple(range(5)), 64)])
+    T = _host_plan(spec).export(0).reshape(-1, D_F)
+    rows = sorted(int(x) for x in T[:, 2])
+    assert rows == [8] * 10 + [16, 16, 64, 64]
 
 
 def test_prefix_plan_rejects_bad_groups():
@@ -174,7 +183,7 @@ def test_page_table_shares_prefix_pages():
         inputs.page_table(_spec("p3", 16, 2, [32, 80], [((0, 1), 48)]))
 
 
-@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[5]], ids=lambda c: c[0])
+@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[5], CASES[6]], ids=lambda c: c[0])
 def test_lists_reproduce_the_oracle(case):
     """Execute the packed lists with the oracle's split and merge arithmetic."""
     name, hq, hkv, dkv, groups = case
