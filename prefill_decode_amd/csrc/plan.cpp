@@ -339,28 +339,37 @@ void build_prefix_lists(const Batch& b, const std::vector<int32_t>& group_of,
     if (group_of[i] >= 0) groups[group_of[i]].m.push_back(i);
   for (int32_t i = 0; i < nd; ++i)
     if (group_of[i] < 0) groups.push_back(G{{i}, 0});
-  // split length: about two units per decode wavefront, at least
-  // kMinDecodeChunk keys; a prefix tile holds all four wavefronts of its
-  // workgroup for its keys
-  double keys = 0.0;
+  // Split lengths.  Suffix units: about two per decode wavefront, at least
+  // kMinDecodeChunk keys (as decode units are sized).  Prefix tiles are
+  // claimed first, so they take a share of the workgroup slots equal to
+  // their share of the work, a tile's wave-key counted at kPrefixTileWeight
+  // of a suffix unit's (its four waves share every K/V load): tile and
+  // suffix work then end together.
+  double tile_keys = 0.0, sfx_keys = 0.0;
   for (const G& gr : groups) {
     if (gr.m.empty()) continue;
     for (int32_t qc = 0; qc < qchunks; ++qc) {
       const int32_t nh = std::min(kDecodeRows, g - qc * kDecodeRows);
-      keys += double(gr.plen) * hkv * kWavesPerWG *
-              (double)ceil_div((int64_t)gr.m.size(), per_tile(nh));
+      tile_keys += double(gr.plen) * hkv * (double)ceil_div((int64_t)gr.m.size(), per_tile(nh));
     }
-    for (int32_t r : gr.m) keys += double(b.dkv[r] - gr.plen) * hkv * qchunks;
+    for (int32_t r : gr.m) sfx_keys += double(b.dkv[r] - gr.plen) * hkv * qchunks;
   }
-  int64_t chunk = kMinDecodeChunk;
-  if (decode_wave_slots > 0 && keys > 0)
+  const double tile_work = kPrefixTileWeight * kWavesPerWG * tile_keys;
+  int64_t chunk = kMinDecodeChunk, chunk_p = kMinDecodeChunk;
+  if (decode_wave_slots > 0 && tile_work + sfx_keys > 0) {
+    const double keys = kWavesPerWG * tile_keys + sfx_keys;
     chunk = std::max<int64_t>(chunk, ceil_div((int64_t)std::ceil(keys / (2.0 * decode_wave_slots)),
                                               kDecodeStep) * kDecodeStep);
+    const double wg_slots = double(decode_wave_slots) / kWavesPerWG;
+    const double tiles = std::max(1.0, wg_slots * tile_work / (tile_work + sfx_keys));
+    chunk_p = std::max<int64_t>(kDecodeStep, ceil_div((int64_t)std::ceil(tile_keys / tiles),
+                                                      kDecodeStep) * kDecodeStep);
+  }
   constexpr int32_t kMaxSegSplits = kMaxMergeSplits / 2;   // prefix + suffix <= 64
-  auto splits_of = [&](int32_t len) -> std::pair<int32_t, int32_t> {   // (count, keys per split)
+  auto splits_of = [&](int32_t len, int64_t ch) -> std::pair<int32_t, int32_t> {   // (count, keys per split)
     if (len <= 0) return {0, 0};
     const int32_t steps = (int32_t)ceil_div(len, kDecodeStep);
-    int64_t s = force_d_splits > 0 ? force_d_splits : ceil_div(len, chunk);
+    int64_t s = force_d_splits > 0 ? force_d_splits : ceil_div(len, ch);
     s = std::max<int64_t>(1, std::min<int64_t>({s, (int64_t)kMaxSegSplits, (int64_t)steps}));
     const int32_t per = (int32_t)ceil_div(steps, s) * kDecodeStep;
     return {(int32_t)ceil_div(len, per), per};
@@ -374,9 +383,9 @@ void build_prefix_lists(const Batch& b, const std::vector<int32_t>& group_of,
     if (gr.m.empty()) continue;
     const int32_t moff = (int32_t)members->size();
     members->insert(members->end(), gr.m.begin(), gr.m.end());
-    const auto [sp, pp] = splits_of(gr.plen);
+    const auto [sp, pp] = splits_of(gr.plen, chunk_p);
     int32_t ss_max = 0;
-    for (int32_t r : gr.m) ss_max = std::max(ss_max, splits_of(b.dkv[r] - gr.plen).first);
+    for (int32_t r : gr.m) ss_max = std::max(ss_max, splits_of(b.dkv[r] - gr.plen, chunk).first);
     const int32_t smax = sp + ss_max;
     const int32_t gbase = n_partials;
     n_partials += (int32_t)gr.m.size() * hq * smax;
@@ -402,7 +411,7 @@ void build_prefix_lists(const Batch& b, const std::vector<int32_t>& group_of,
         // suffixes
         for (int32_t rl = 0; rl < nm; ++rl) {
           const int32_t r = gr.m[rl];
-          const auto [ss, ps] = splits_of(b.dkv[r] - gr.plen);
+          const auto [ss, ps] = splits_of(b.dkv[r] - gr.plen, chunk);
           for (int32_t k = 0; k < ss; ++k) {
             const int32_t kb = gr.plen + k * ps, ke = std::min(b.dkv[r], gr.plen + (k + 1) * ps);
             DI it;
@@ -414,7 +423,7 @@ void build_prefix_lists(const Batch& b, const std::vector<int32_t>& group_of,
         }
       }
     for (int32_t rl = 0; rl < nm; ++rl) {
-      const int32_t n = sp + splits_of(b.dkv[gr.m[rl]] - gr.plen).first;
+      const int32_t n = sp + splits_of(b.dkv[gr.m[rl]] - gr.plen, chunk).first;
       for (int32_t h = 0; h < hq; ++h) {
         w.m_tasks.push_back(gr.m[rl] * hq + h);
         w.m_tasks.push_back(region(rl, h));

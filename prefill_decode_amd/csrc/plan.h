@@ -25,6 +25,11 @@ constexpr int kPrefillKeys = 64;    // keys per prefill KV tile
 constexpr int kDecodeStep = 32;     // keys per decode step (2 MFMA key blocks)
 constexpr int kDecodeRows = 16;     // decode query tile (MFMA 16 rows)
 constexpr int kPrefixTileRows = 64; // shared-prefix tile: 4 waves x 16 rows
+// Cost of one wave-key of a shared-prefix tile relative to a suffix unit's,
+// for sizing tile splits (measured: on five shared-prefix shapes, from a long
+// shared prefix with short suffixes to the reverse, the tile count this
+// weight predicts was the fastest or within 3% of it)
+constexpr double kPrefixTileWeight = 0.5;
 constexpr int kWavesPerWG = 4;
 constexpr int kMaxXcds = 16;
 constexpr int kMaxPrefillSplits = 16;

@@ -144,7 +144,7 @@ def test_prefix_units_are_shared_by_the_pack():
     # g = 24 (a partial block of 8 heads per KV head): full blocks pack four
     # members, the partial block one member per tile
     spec = _spec("g24", 48, 2, [64] * 5, [(tuple(range(5)), 64)])
-    T = _host_plan(spec).export(0).reshape(-1, D_F)
+    T = _host_plan(spec, decode_kv_splits=1).export(0).reshape(-1, D_F)
     rows = sorted(int(x) for x in T[:, 2])
     assert rows == [8] * 10 + [16, 16, 64, 64]
 
@@ -166,6 +166,20 @@ def test_prefix_plan_rejects_bad_groups():
     with pytest.raises(B.PodError, match=B.STATUS[2]):
         B.plan_shared_prefix_host(p, [64, 80], [0, 0], [64],
                                   B.make_tuning(flags=B.FLAG_BATCHED_PREFILL))
+
+
+def test_tile_splits_follow_the_work_share():
+    # 128 base tiles (16 groups x 8 KV heads); 512 workgroup slots.  Tiles take
+    # the slots' share that their work has (a tile wave-key at half a suffix
+    # unit's): a long prefix with short suffixes fills every slot, a short
+    # prefix with long suffixes keeps one tile per pack
+    def count(plen, own):
+        groups = [(tuple(range(8 * g, 8 * g + 8)), plen) for g in range(16)]
+        spec = _spec("w", 64, 8, [plen + own] * 128, groups)
+        return _host_plan(spec).info()["prefill_items"]
+    assert count(4096, 64) == 512
+    assert count(2048, 544) == 256
+    assert count(512, 2560) == 128
 
 
 def test_page_table_shares_prefix_pages():
