@@ -3,7 +3,8 @@
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-flush] [--no-cpu]
                     [--no-per-config] [--config-steps K2]
     python bench.py --pmc-run [--config NAME]          (driver for rocprofv3 counter runs)
-    python bench.py --summarize-pmc DIR [--config NAME] (writes profiles/traffic_*.md)
+    python bench.py --summarize-ea DIR [--config NAME]  (writes profiles/traffic_*.md)
+    python bench.py --summarize-counters DIR [--config NAME] (writes profiles/counters_*.md)
     python bench.py --summarize-stats DIR [--config NAME] (writes profiles/*_stats.md)
 
 A step is one pass of the hot path over the batch: pod_attn_run, i.e. the fused
@@ -195,119 +196,162 @@ def pmc_run(args):
           f"one {COPY_BYTES} B copy", flush=True)
 
 
-def summarize_pmc(args):
-    """Reads the FETCH_SIZE / WRITE_SIZE passes under DIR (DIR/fetch, DIR/write)
-    and writes profiles/traffic_pod_fused_kernel_<config>.md."""
+# HBM traffic from the L2-to-memory request counters, in bytes by request
+# size (no calibration): one pass for reads, one for writes
+EA_READ = ["TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum",
+           "TCC_EA0_RDREQ_sum"]
+EA_WRITE = ["TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_sum"]
+KERNELS = ("pod_fused_kernel", "pod_prefill_kernel", "pod_decode_kernel", "pod_decode_pack_kernel",
+           "pod_decode_fp8_kernel", "pod_merge_kernel")
+
+
+def _kernel_key(name):
+    for k in KERNELS:
+        if k in name:
+            return k
+    return "copy" if "copy" in name.lower() else None
+
+
+def _load_counters(root):
+    """{kernel: {counter: [value per dispatch]}} from every counter CSV under root."""
     import csv
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))
+    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            k = _kernel_key(row["Kernel_Name"])
+            if k is not None:
+                vals[k][row["Counter_Name"]].append(float(row["Counter_Value"]))
+    return vals
 
-    def load(sub, counter):
-        vals, copy = [], []
-        for f in glob.glob(os.path.join(args.summarize_pmc, sub, "**", "*counter_collection.csv"),
-                           recursive=True):
-            for row in csv.DictReader(open(f)):
-                if row.get("Counter_Name") != counter:
-                    continue
-                name, v = row["Kernel_Name"], float(row["Counter_Value"])
-                if "pod_fused_kernel" in name:
-                    vals.append(v)
-                elif "copy" in name.lower():
-                    copy.append(v)
-        return vals, copy
 
-    fv, fc = load("fetch", "FETCH_SIZE")
-    wv, wc = load("write", "WRITE_SIZE")
-    if not (fv and wv and fc and wc):
-        sys.exit("summarize-pmc: missing fused or copy dispatches in the counter CSVs")
-    f_copy, w_copy = max(fc), max(wc)                      # the 1 GiB copy
-    kf, kw = COPY_BYTES / f_copy, COPY_BYTES / w_copy       # bytes per counter unit
-    f_b, w_b = float(np.mean(fv)) * kf, float(np.mean(wv)) * kw
+def summarize_ea(args):
+    """Reads the EA_READ pass (DIR/rd) and the EA_WRITE pass (DIR/wr) over
+    `--pmc-run` and writes profiles/traffic_pod_fused_kernel_<config>.md: HBM
+    bytes per dispatch of every kernel, from request counts times request
+    sizes; the 1 GiB copy of the same process checks the arithmetic."""
+    rd, wr = _load_counters(os.path.join(args.summarize_ea, "rd")), \
+        _load_counters(os.path.join(args.summarize_ea, "wr"))
+
+    def rbytes(v, i):
+        c32, c64, c128, tot = (v[c][i] for c in EA_READ)
+        return 32 * c32 + 64 * c64 + 128 * c128, tot - c32 - c64 - c128
+
+    def wbytes(v, i):
+        c64, tot = (v[c][i] for c in EA_WRITE)
+        return 64 * c64 + 32 * (tot - c64)
+
+    fused = "pod_fused_kernel" if "pod_fused_kernel" in rd else "pod_decode_pack_kernel" \
+        if "pod_decode_pack_kernel" in rd else "pod_decode_fp8_kernel"
+    if fused not in rd or fused not in wr or "copy" not in rd or "copy" not in wr:
+        sys.exit("summarize-ea: missing kernel or copy dispatches in the counter CSVs")
+    rows, res = [], {}
+    for k in (fused,) + tuple(x for x in KERNELS if x != fused) + ("copy",):
+        if k not in rd or k not in wr:
+            continue
+        r = [rbytes(rd[k], i) for i in range(len(rd[k][EA_READ[0]]))]
+        w = [wbytes(wr[k], i) for i in range(len(wr[k][EA_WRITE[0]]))]
+        if k == "copy":
+            # the 1 GiB copy: the largest of the copy-like dispatches (torch's
+            # own fills and conversions also match the name)
+            r, w = [max(r, key=lambda x: x[0])], [max(w)]
+        n = min(len(r), len(w))
+        rb, wb = float(np.mean([x[0] for x in r])), float(np.mean(w))
+        other = int(max(x[1] for x in r))
+        res[k] = (rb, wb)
+        rows.append(f"| `{k}` | {n} | {rb / 1e6:.2f} | {wb / 1e6:.2f} | {other} |")
     from prefill_decode_amd import inputs, metrics
     spec = inputs.config_spec(args.config, n_dec=args.n_dec)
     alg = metrics.algorithmic_counts(spec)["bytes"]
-    d = os.path.abspath(args.summarize_pmc)
-    txt = f"""# HBM traffic of pod_fused_kernel — {DESCR.get(args.config, args.config)}
+    f_b, w_b = res[fused]
+    c_r, c_w = res["copy"]
+    txt = f"""# HBM traffic — {DESCR.get(args.config, args.config)}
 
-Two `rocprofv3 --pmc` passes (one counter each) over `bench.py --pmc-run`:
-{args.steps} fused runs of the batch (then as many sequential runs, not used here) and one plain
-{COPY_BYTES}-byte device-to-device copy. The copy's
-counters calibrate them: bytes per counter unit = {COPY_BYTES} / (the copy's reading).
+Two `rocprofv3 --pmc` passes over `bench.py --pmc-run` ({args.steps} runs of `pod_attn_run`, as
+many of `pod_attn_sequential_run`, then one plain {COPY_BYTES}-byte device-to-device copy). Bytes
+are the L2-to-memory requests times their sizes: reads 32 B x `TCC_EA0_RDREQ_32B` + 64 B x
+`TCC_EA0_RDREQ_64B` + 128 B x `TCC_EA0_RDREQ_128B` (the last column counts read requests of any
+other size: 0 means the three sizes cover every request), writes 64 B x `TCC_EA0_WRREQ_64B` + 32 B x
+the rest. The copy reads and writes {COPY_BYTES / 1e6:.2f} MB by construction; measured here:
+{c_r / 1e6:.2f} MB read, {c_w / 1e6:.2f} MB written.
 
 Commands (from the repository root; `$D` = a scratch directory):
 
     cd /tmp && export TMPDIR=/tmp
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d $D/fetch -o run -- python3 bench.py --pmc-run --config {args.config} --steps {args.steps}
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d $D/write -o run -- python3 bench.py --pmc-run --config {args.config} --steps {args.steps}
-    python3 bench.py --summarize-pmc $D --config {args.config} --steps {args.steps}
+    rocprofv3 --pmc {" ".join(EA_READ)} --output-format csv -d $D/rd -o run -- python3 bench.py --pmc-run --config {args.config} --steps {args.steps}
+    rocprofv3 --pmc {" ".join(EA_WRITE)} --output-format csv -d $D/wr -o run -- python3 bench.py --pmc-run --config {args.config} --steps {args.steps}
+    python3 bench.py --summarize-ea $D --config {args.config} --steps {args.steps}
 
-| quantity | value |
-|---|---|
-| copy FETCH_SIZE (counter units) | {f_copy:.6g} |
-| copy WRITE_SIZE (counter units) | {w_copy:.6g} |
-| bytes per FETCH_SIZE unit | {kf:.6g} |
-| bytes per WRITE_SIZE unit | {kw:.6g} |
-| fused FETCH_SIZE per dispatch, mean of {len(fv)} | {np.mean(fv):.6g} |
-| fused WRITE_SIZE per dispatch, mean of {len(wv)} | {np.mean(wv):.6g} |
-| HBM read bytes per fused launch | {f_b:.6g} |
-| HBM write bytes per fused launch | {w_b:.6g} |
-| algorithmic bytes of the batch | {alg:.6g} |
-| traffic / algorithmic | {(f_b + w_b) / alg:.4f} |
+| kernel | dispatches | read MB / dispatch | written MB / dispatch | other-size read requests |
+|---|---|---|---|---|
+""" + "\n".join(rows) + f"""
 
+Algorithmic bytes of the batch (each Q/K/V/O/LSE byte once): {alg / 1e6:.2f} MB; traffic of
+`{fused}` / algorithmic = {(f_b + w_b) / alg:.4f}.
+
+- kernel: `{fused}`
 - traffic_bytes_per_launch: `{f_b + w_b:.6g}`
 - sources_sha256: `{sources_digest()}`
 """
     os.makedirs(PROFILES, exist_ok=True)
     open(traffic_file(args.config), "w").write(txt)
     print(txt)
-    del d
 
 
-COUNTERS = ["MfmaUtil", "LdsBankConflict", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"]
+COUNTERS = ["MfmaUtil", "VALUBusy", "LdsBankConflict", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"]
+# instruction mix per kernel (one pass)
+INST_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS",
+                 "SQ_INSTS_SALU", "SQ_INSTS_VMEM", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES"]
 
 
 def summarize_counters(args):
-    """Reads one `rocprofv3 --pmc` pass of COUNTERS over `--pmc-run` under DIR
-    and writes profiles/counters_<config>.md: MFMA busy share of SIMD cycles
-    and LDS bank conflicts per kernel (means over dispatches)."""
-    import csv
-    from collections import defaultdict
-
-    vals = defaultdict(lambda: defaultdict(list))
-    for f in glob.glob(os.path.join(args.summarize_counters, "**", "*counter_collection.csv"),
-                       recursive=True):
-        for row in csv.DictReader(open(f)):
-            name = row["Kernel_Name"]
-            for k in ("pod_fused_kernel", "pod_prefill_kernel", "pod_decode_kernel",
-                      "pod_merge_kernel"):
-                if k in name:
-                    vals[k][row["Counter_Name"]].append(float(row["Counter_Value"]))
-    if "pod_fused_kernel" not in vals:
-        sys.exit("summarize-counters: no fused-kernel dispatches in the counter CSVs")
-    lines = []
-    for k in ("pod_fused_kernel", "pod_prefill_kernel", "pod_decode_kernel", "pod_merge_kernel"):
-        if k not in vals:
+    """Reads the COUNTERS pass (DIR/util) and the INST_COUNTERS pass
+    (DIR/inst) over `--pmc-run` and writes profiles/counters_<config>.md: MFMA
+    and VALU busy shares, LDS bank conflicts and the instruction mix per
+    kernel (means over dispatches)."""
+    util = _load_counters(os.path.join(args.summarize_counters, "util"))
+    inst = _load_counters(os.path.join(args.summarize_counters, "inst"))
+    if not util:
+        sys.exit("summarize-counters: no kernel dispatches in the counter CSVs")
+    lines, mix = [], []
+    for k in KERNELS:
+        if k not in util:
             continue
-        v = vals[k]
+        v = util[k]
         mean = lambda c: float(np.mean(v[c])) if v.get(c) else float("nan")
         lines.append(f"| `{k}` | {len(v.get('MfmaUtil', []))} | {mean('MfmaUtil'):.1f} | "
-                     f"{mean('LdsBankConflict'):.4f} | {mean('SQ_LDS_BANK_CONFLICT'):.4g} | "
-                     f"{mean('SQ_LDS_IDX_ACTIVE'):.4g} |")
-    cnt = " ".join(COUNTERS)
-    txt = f"""# MFMA busy and LDS bank conflicts — {DESCR.get(args.config, args.config)}
+                     f"{mean('VALUBusy'):.1f} | {mean('LdsBankConflict'):.4f} | "
+                     f"{mean('SQ_LDS_BANK_CONFLICT'):.4g} | {mean('SQ_LDS_IDX_ACTIVE'):.4g} |")
+        if k in inst:
+            u = inst[k]
+            im = lambda c: float(np.mean(u[c])) if u.get(c) else float("nan")
+            mf = im("SQ_INSTS_MFMA")
+            mix.append(f"| `{k}` | {mf:.4g} | {im('SQ_INSTS_VALU'):.4g} | "
+                       f"{im('SQ_INSTS_VALU_TRANS_F32'):.4g} | {im('SQ_INSTS_LDS'):.4g} | "
+                       f"{im('SQ_INSTS_SALU'):.4g} | {im('SQ_INSTS_VMEM'):.4g} | "
+                       f"{(im('SQ_INSTS_VALU') - mf) / mf if mf > 0 else float('nan'):.2f} |")
+    txt = f"""# MFMA and VALU busy, LDS bank conflicts, instruction mix — {DESCR.get(args.config, args.config)}
 
-One `rocprofv3 --pmc` pass over `bench.py --pmc-run` ({args.steps} fused runs, then {args.steps}
-sequential runs). `MfmaUtil` = MFMA-busy cycles summed over SIMDs / (GPU-active cycles × SIMDs), in
-percent, for the whole launch (idle SIMDs, launch ramp and tail included). `LdsBankConflict` =
-bank-conflict cycles / conflict-free LDS cycles.
+Two `rocprofv3 --pmc` passes over `bench.py --pmc-run` ({args.steps} runs of `pod_attn_run`, then
+{args.steps} of `pod_attn_sequential_run`). `MfmaUtil` / `VALUBusy` = MFMA-busy / VALU-active cycles
+summed over SIMDs / (GPU-active cycles x SIMDs), in percent, for the whole launch (idle SIMDs, launch
+ramp and tail included). `LdsBankConflict` = bank-conflict cycles / conflict-free LDS cycles.
+Instruction counts are per dispatch, summed over waves (`SQ_INSTS_VALU` includes the MFMAs).
 
 Commands (from the repository root; `$D` = a scratch directory):
 
     cd /tmp && export TMPDIR=/tmp
-    rocprofv3 --pmc {cnt} --output-format csv -d $D -o run -- python3 bench.py --pmc-run --config {args.config} --steps {args.steps}
+    rocprofv3 --pmc {" ".join(COUNTERS)} --output-format csv -d $D/util -o run -- python3 bench.py --pmc-run --config {args.config} --steps {args.steps}
+    rocprofv3 --pmc {" ".join(INST_COUNTERS)} --output-format csv -d $D/inst -o run -- python3 bench.py --pmc-run --config {args.config} --steps {args.steps}
     python3 bench.py --summarize-counters $D --config {args.config} --steps {args.steps}
 
-| kernel | dispatches | MfmaUtil % | LdsBankConflict | SQ_LDS_BANK_CONFLICT | SQ_LDS_IDX_ACTIVE |
-|---|---|---|---|---|---|
-""" + "\n".join(lines) + f"""
+| kernel | dispatches | MfmaUtil % | VALUBusy % | LdsBankConflict | SQ_LDS_BANK_CONFLICT | SQ_LDS_IDX_ACTIVE |
+|---|---|---|---|---|---|---|
+""" + "\n".join(lines) + """
+
+| kernel | MFMA instrs | VALU instrs | of which exp/log (trans f32) | LDS instrs | SALU instrs | VMEM instrs | non-MFMA VALU per MFMA |
+|---|---|---|---|---|---|---|---|
+""" + "\n".join(mix) + f"""
 
 - sources_sha256: `{sources_digest()}`
 """
@@ -341,7 +385,7 @@ steps; each step runs `pod_attn_run` and `pod_attn_sequential_run`, each after a
 Commands (from the repository root; `$D` = a scratch directory):
 
     cd /tmp && export TMPDIR=/tmp
-    rocprofv3 --kernel-trace --stats --output-format csv -d $D -o run -- python3 bench.py --config {args.config} --steps {args.steps} --warmup {args.warmup} --no-cpu
+    rocprofv3 --kernel-trace --stats --output-format csv -d $D -o run -- python3 bench.py --config {args.config} --steps {args.steps} --warmup {args.warmup} --no-cpu --no-per-config
     python3 bench.py --summarize-stats $D --config {args.config} --steps {args.steps} --warmup {args.warmup}
 
 | kernel | calls | avg µs | min µs | max µs | % of GPU time |
@@ -538,21 +582,21 @@ def main():
     ap.add_argument("--sched", type=int, default=0,
                     help="0 auto, 1 co-locate on every CU, 2 ordered, 3 CU partition")
     ap.add_argument("--pmc-run", action="store_true")
-    ap.add_argument("--summarize-pmc", default=None, metavar="DIR")
     ap.add_argument("--summarize-stats", default=None, metavar="DIR")
     ap.add_argument("--summarize-counters", default=None, metavar="DIR")
+    ap.add_argument("--summarize-ea", default=None, metavar="DIR")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(sharded by KV head or by request, each GPU would run this same kernel on its "
               "share with no exchange; this library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
-    if args.summarize_pmc:
-        return summarize_pmc(args)
     if args.summarize_stats:
         return summarize_stats(args)
     if args.summarize_counters:
         return summarize_counters(args)
+    if args.summarize_ea:
+        return summarize_ea(args)
     if args.pmc_run:
         return pmc_run(args)
 

@@ -127,6 +127,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF,
                                            0x00020000);
 }
+// The same over `bytes` bytes: a load at a larger offset returns zeros (and
+// an LDS DMA deposits them) instead of reading memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_n(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
 // cache policy bits of buffer loads: 0 = default, kStream = non-temporal
 // (data read once, e.g. a decode request's KV, should not displace reused lines)
 constexpr int kStream = 2;
@@ -312,9 +317,12 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
       }
     }
   };
-  // resource of this wave's (clamped) 16-key block of tile t
+  // resource of this wave's (clamped) 16-key block of tile t, bounded to
+  // the block's keys up to kv_end - 1: rows past them read as zeros
   auto block_rsrc = [&](int t, const char* gbase) {
-    return rsrc(gbase + (KVM != KV_PAGED_NARROW ? addr.block_row(bstart(t)) : 0) * tok);
+    const int b0 = bstart(t);
+    return rsrc_n(gbase + (KVM != KV_PAGED_NARROW ? addr.block_row(b0) : 0) * tok,
+                  min(kv_end - b0, 16) * (int)tok);
   };
 
   // per-lane LDS read offsets (bytes from a tile's base); the half h and
@@ -405,12 +413,11 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   // sum into l.  k-step ks uses registers 8 ks .. 8 ks + 7.
   auto expsum = [&](f32x16& sx, float m, float& l, u32x4 (&p)[2]) {
     const float nm = m == kNegInf ? 0.0f : -m;
-    float ls = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sx[r] = exp2_(__builtin_fmaf(sx[r], sl2, nm));
-      ls += sx[r];
-    }
+    for (int r = 0; r < 16; ++r) sx[r] = exp2_(__builtin_fmaf(sx[r], sl2, nm));
+    float ls = sx[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) ls += sx[r];
     l += ls;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -485,16 +492,22 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   stage(0, true, 0, rk);
   stage(0, false, 0, rv);
   // DMA of row group i (rows 4i .. 4i + 3 of this wave's 16) of tile t into
-  // buffers `buf`, without branches (clamped rows), so that it can sit
-  // among a half's MFMAs
-  auto dma_row = [&](int t, bool is_k, int buf, __amdgpu_buffer_rsrc_t r, int i) {
-    int sl = threadIdx.x;
-    asm volatile("" : "+v"(sl));
-    const int dq = (sl >> 4) & 3, dc = sl & 15;
+  // buffers `buf`, without branches, so that it can sit among a half's
+  // MFMAs: rows past the last key read as zeros (the block's resource ends
+  // there).  Lane L takes row rr = 4i + dq (dq = L/16 % 4) and source chunk
+  // dc ^ swz(rr) (dc = L%16).  K's swizzle rr & 15 makes that (dc ^ dq) ^ 4i;
+  // V's depends on i only through i & 1 and flips bit 1 with it.  So two
+  // lane offsets held across the item give every row group's offset in one
+  // VALU (they pass through an empty asm per use, so that the eight
+  // derived offsets are not hoisted and held as well).
+  const int ldq = (lane >> 4) & 3, ldc = lane & 15;
+  const uint32_t dma_k0 = (uint32_t)ldq * tok + 16u * (uint32_t)(ldc ^ ldq);
+  const uint32_t dma_v0 = (uint32_t)ldq * tok + 16u * (uint32_t)(ldc ^ vswz(ldq));
+  auto dma_row = [&](bool is_k, int buf, __amdgpu_buffer_rsrc_t r, int i) {
     char* dst = (is_k ? (buf ? kt1 : kt0) : (buf ? vt1 : vt0)) + wrow;
-    const int rmax = kv_end - 1 - bstart(t);
-    const int rr = 4 * i + dq;
-    const uint32_t vo = (uint32_t)min(rr, rmax) * tok + 16u * (dc ^ (is_k ? kswz(rr) : vswz(rr)));
+    uint32_t b = is_k ? dma_k0 : dma_v0;
+    asm volatile("" : "+v"(b));
+    const uint32_t vo = (b ^ (is_k ? 64u * i : (i & 1) ? 32u : 0u)) + 4u * i * tok;
     dma16(r, dst + 4 * i * kRowBytes, vo, 0);
   };
   auto nothing = [](int) {};
@@ -527,8 +540,8 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
       // double the live ranges the register allocator has to cover)
       const bool masked = t >= t_mask;
       if (KVM != KV_PAGED_NARROW)
-        half(t, 0, kb, vb, masked, [&](int i) { dma_row(tn, true, P ^ 1, rk, i); },
-             [&](int i) { dma_row(tn, false, P ^ 1, rv, i); });
+        half(t, 0, kb, vb, masked, [&](int i) { dma_row(true, P ^ 1, rk, i); },
+             [&](int i) { dma_row(false, P ^ 1, rv, i); });
       else
         half(t, 0, kb, vb, masked, nothing, nothing);
       if (h1) half(t, 1, kb, vb, masked, nothing, nothing);
