@@ -83,15 +83,24 @@ def sources_digest():
     return h.hexdigest()[:16]
 
 
-def traffic_file(config):
-    return os.path.join(PROFILES, f"traffic_pod_fused_kernel_{config}.md")
+def main_kernel(spec):
+    """The kernel pod_attn_run launches for this workload (the roofline's)."""
+    if spec.prefix_groups:
+        return "pod_decode_pack_kernel"
+    if spec.kv_dtype == "fp8_e4m3":
+        return "pod_decode_fp8_kernel"
+    return "pod_fused_kernel"
 
 
-def read_traffic(config):
-    """HBM bytes per fused launch from the committed counter summary, or None
-    when there is none or the kernel sources changed since it was taken."""
+def traffic_file(config, kernel):
+    return os.path.join(PROFILES, f"traffic_{kernel}_{config}.md")
+
+
+def read_traffic(config, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or the kernel sources changed since it was taken."""
     try:
-        lines = open(traffic_file(config)).read().splitlines()
+        lines = open(traffic_file(config, kernel)).read().splitlines()
     except OSError:
         return None
     kv = {}
@@ -213,15 +222,24 @@ def _kernel_key(name):
 
 
 def _load_counters(root):
-    """{kernel: {counter: [value per dispatch]}} from every counter CSV under root."""
+    """{kernel: {counter: [value per dispatch, in dispatch order]}} from every
+    counter CSV under root.  "copy" keeps only the last copy-like dispatch:
+    the 1 GiB copy that ends `--pmc-run` (torch's own conversions and fills
+    before it match the name too)."""
     import csv
     from collections import defaultdict
-    vals = defaultdict(lambda: defaultdict(list))
+    rows = defaultdict(lambda: defaultdict(list))
     for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
         for row in csv.DictReader(open(f)):
             k = _kernel_key(row["Kernel_Name"])
             if k is not None:
-                vals[k][row["Counter_Name"]].append(float(row["Counter_Value"]))
+                rows[k][row["Counter_Name"]].append((int(row["Dispatch_Id"]),
+                                                     float(row["Counter_Value"])))
+    vals = defaultdict(dict)
+    for k, cs in rows.items():
+        for c, v in cs.items():
+            v = sorted(v)
+            vals[k][c] = [v[-1][1]] if k == "copy" else [x[1] for x in v]
     return vals
 
 
@@ -241,8 +259,9 @@ def summarize_ea(args):
         c64, tot = (v[c][i] for c in EA_WRITE)
         return 64 * c64 + 32 * (tot - c64)
 
-    fused = "pod_fused_kernel" if "pod_fused_kernel" in rd else "pod_decode_pack_kernel" \
-        if "pod_decode_pack_kernel" in rd else "pod_decode_fp8_kernel"
+    from prefill_decode_amd import inputs, metrics
+    spec = inputs.config_spec(args.config, n_dec=args.n_dec)
+    fused = main_kernel(spec)
     if fused not in rd or fused not in wr or "copy" not in rd or "copy" not in wr:
         sys.exit("summarize-ea: missing kernel or copy dispatches in the counter CSVs")
     rows, res = [], {}
@@ -251,17 +270,11 @@ def summarize_ea(args):
             continue
         r = [rbytes(rd[k], i) for i in range(len(rd[k][EA_READ[0]]))]
         w = [wbytes(wr[k], i) for i in range(len(wr[k][EA_WRITE[0]]))]
-        if k == "copy":
-            # the 1 GiB copy: the largest of the copy-like dispatches (torch's
-            # own fills and conversions also match the name)
-            r, w = [max(r, key=lambda x: x[0])], [max(w)]
         n = min(len(r), len(w))
         rb, wb = float(np.mean([x[0] for x in r])), float(np.mean(w))
         other = int(max(x[1] for x in r))
         res[k] = (rb, wb)
         rows.append(f"| `{k}` | {n} | {rb / 1e6:.2f} | {wb / 1e6:.2f} | {other} |")
-    from prefill_decode_amd import inputs, metrics
-    spec = inputs.config_spec(args.config, n_dec=args.n_dec)
     alg = metrics.algorithmic_counts(spec)["bytes"]
     f_b, w_b = res[fused]
     c_r, c_w = res["copy"]
@@ -294,7 +307,7 @@ Algorithmic bytes of the batch (each Q/K/V/O/LSE byte once): {alg / 1e6:.2f} MB;
 - sources_sha256: `{sources_digest()}`
 """
     os.makedirs(PROFILES, exist_ok=True)
-    open(traffic_file(args.config), "w").write(txt)
+    open(traffic_file(args.config, fused), "w").write(txt)
     print(txt)
 
 
@@ -362,19 +375,29 @@ Commands (from the repository root; `$D` = a scratch directory):
 
 def summarize_stats(args):
     """Reads a `rocprofv3 --kernel-trace --stats --output-format csv` run under
-    DIR and writes profiles/pod_fused_kernel_<config>_stats.md."""
+    DIR and writes profiles/<kernel>_<config>_stats.md."""
     import csv
 
     files = glob.glob(os.path.join(args.summarize_stats, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         sys.exit("summarize-stats: no kernel_stats.csv under " + args.summarize_stats)
     rows = list(csv.DictReader(open(files[0])))
+    # per-dispatch durations from the trace of the same run (for the median,
+    # which the bench's kernel time is too)
+    durs = {}
+    for f in glob.glob(os.path.join(args.summarize_stats, "**", "*kernel_trace.csv"),
+                       recursive=True):
+        for r in csv.DictReader(open(f)):
+            durs.setdefault(r["Kernel_Name"], []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = []
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         name = r["Name"].split("(")[0].replace("void ", "")
         if len(name) > 70:
             name = name[:67] + "..."
-        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+        med = durs.get(r["Name"])
+        med = f"{float(np.median(med)):.1f}" if med else "-"
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {med} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['Percentage']):.1f} |")
     txt = f"""# Kernel times — {DESCR.get(args.config, args.config)}
@@ -385,17 +408,19 @@ steps; each step runs `pod_attn_run` and `pod_attn_sequential_run`, each after a
 Commands (from the repository root; `$D` = a scratch directory):
 
     cd /tmp && export TMPDIR=/tmp
-    rocprofv3 --kernel-trace --stats --output-format csv -d $D -o run -- python3 bench.py --config {args.config} --steps {args.steps} --warmup {args.warmup} --no-cpu --no-per-config
+    rocprofv3 --kernel-trace --stats --output-format csv -d $D -o run -- python3 bench.py --config {args.config} --steps {args.steps} --warmup {args.warmup} --no-cpu --no-per-config --paths fused,seq
     python3 bench.py --summarize-stats $D --config {args.config} --steps {args.steps} --warmup {args.warmup}
 
-| kernel | calls | avg µs | min µs | max µs | % of GPU time |
-|---|---|---|---|---|---|
+| kernel | calls | avg µs | median µs | min µs | max µs | % of GPU time |
+|---|---|---|---|---|---|---|
 """ + "\n".join(lines) + f"""
 
 - sources_sha256: `{sources_digest()}`
 """
     os.makedirs(PROFILES, exist_ok=True)
-    out = os.path.join(PROFILES, f"pod_fused_kernel_{args.config}_stats.md")
+    from prefill_decode_amd import inputs
+    kernel = main_kernel(inputs.config_spec(args.config, n_dec=args.n_dec))
+    out = os.path.join(PROFILES, f"{kernel}_{args.config}_stats.md")
     open(out, "w").write(txt)
     print(txt)
 
@@ -496,6 +521,11 @@ def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup,
     """Times every path on one workload; returns (runner, fields)."""
     if spec is None:
         spec = inputs.config_spec(name, n_dec=n_dec)
+    if spec.prefix_groups:
+        # a shared-prefix plan runs the packed path fused and the unshared
+        # decode on the sequential and streams paths; it has no batched or
+        # ordered variant
+        paths = tuple(p for p in paths if p in ("fused", "seq", "streams"))
     batch = inputs.make_batch_device(spec)
     counts = metrics.algorithmic_counts(spec)
     flags = B.FLAG_BATCHED_PREFILL if "batched" in paths else 0
@@ -552,7 +582,7 @@ def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup,
         "achieved_hbm_gbs": counts["bytes"] / t_step / 1e9,
         "algorithmic": {"gflop": counts["flops"] / 1e9, "gbytes": counts["bytes"] / 1e9},
         "achieved_hbm_gbs_kernel": counts["bytes"] / t_kern / 1e9,
-        "traffic_bytes_per_launch": read_traffic(spec.name),
+        "traffic_bytes_per_launch": read_traffic(spec.name, main_kernel(spec)),
         "plan": {"first_call_ms": plan_first_ms, "host_warm_ms": float(np.median(warm)),
                  "prefill_items": info["prefill_items"], "decode_items": info["decode_items"],
                  "merge_tasks": info["merge_tasks"],
@@ -574,6 +604,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-per-config", action="store_true",
                     help="time the headline workload only")
+    ap.add_argument("--paths", default=",".join(PATHS),
+                    help="paths timed on the headline workload (comma-separated subset of "
+                         + ",".join(PATHS) + "; fused and seq are always timed)")
     ap.add_argument("--config-steps", type=int, default=10,
                     help="timed steps per path for the other workloads")
     ap.add_argument("--quarters", type=int, default=-1, help="prefill quarters per CU (-1 auto)")
@@ -612,9 +645,10 @@ def main():
     # ---- the headline workload: exactly --steps timed steps per path ----
     print(f"bench: {args.config} ({args.steps} steps, {args.warmup} warm-up)", file=sys.stderr,
           flush=True)
+    paths = tuple(p for p in PATHS if p in args.paths.split(",") or p in ("fused", "seq"))
     runner, batch, spec, counts, t, kern, head = measure_config(
         torch, B, inputs, metrics, timer, args.config, args.n_dec, args.steps, args.warmup,
-        tuning_kw)
+        tuning_kw, paths=paths)
     wall = timer.last_wall
     # warm (no eviction) back-to-back fused steps
     w0, w1 = timer.ev(), timer.ev()
@@ -635,7 +669,7 @@ def main():
                 "peak": metrics.PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = head["traffic_bytes_per_launch"]
-    roof["kernel"] = "pod_fused_kernel"
+    roof["kernel"] = main_kernel(spec)
     roof["kernel_us"] = t_kern * 1e6
 
     out = {
