@@ -84,11 +84,16 @@ def sources_digest():
 
 
 def main_kernel(spec):
-    """The kernel pod_attn_run launches for this workload (the roofline's)."""
+    """The kernel pod_attn_run launches for this workload (the roofline's): a
+    batch of one kind runs the one kernel it needs."""
     if spec.prefix_groups:
         return "pod_decode_pack_kernel"
     if spec.kv_dtype == "fp8_e4m3":
         return "pod_decode_fp8_kernel"
+    if not spec.prefill_qo_len:
+        return "pod_decode_kernel"
+    if not spec.decode_kv_len:
+        return "pod_prefill_kernel"
     return "pod_fused_kernel"
 
 
@@ -458,15 +463,20 @@ class Timer:
 
     def interleaved(self, calls, steps, warmup):
         """Median-ready times (ms) of each named call, the calls interleaved
-        step by step so that drift hits them alike."""
+        step by step so that drift hits them alike; the order rotates every
+        step, so that each call follows each other one equally often (a heavy
+        call can leave the clocks lower for the next)."""
         for _ in range(warmup):
             for f in calls.values():
                 f()
         self.torch.cuda.synchronize()
         evs = {k: [(self.ev(), self.ev()) for _ in range(steps)] for k in calls}
+        names = list(calls)
         wall0 = time.perf_counter()
         for i in range(steps):
-            for k, f in calls.items():
+            for j in range(len(names)):
+                k = names[(i + j) % len(names)]
+                f = calls[k]
                 self.evict()
                 evs[k][i][0].record(self.stream)
                 f()

@@ -326,9 +326,15 @@ pod_status_t pod_attn_plan_scratch(const pod_attn_params_t* params,
                                    const pod_attn_tuning_t* tuning, hipStream_t stream,
                                    pod_attn_plan_t* out_plan);
 
-/* Fused run: one persistent kernel (two workgroups per CU) for all prefill
- * tiles and decode splits, then the merge kernel if any split exists.
- * Asynchronous on `stream`.
+/* Fused run: one kernel for all prefill tiles and decode splits ([POD] "How
+ * POD-Attention overlaps": prefill and decode in one launch, roles taken per
+ * CU in software) -- persistent, two workgroups per CU, or one workgroup per
+ * unit as the plan chose -- then the merge kernel if any split exists.  A
+ * batch of one kind (no decodes, or no prefill; bf16 or FP8) has nothing to
+ * overlap and runs the one kernel it needs with the sequential plan's lists,
+ * i.e. what pod_attn_sequential_run runs (unless the plan traces: the trace
+ * is indexed by the fused launch's units).  A shared-prefix plan runs its
+ * packed decode kernel.  Asynchronous on `stream`.
  * Errors: POD_ERR_INVALID_ARGUMENT (NULL plan/tensors, a required pointer
  * NULL or not 16-byte aligned, plan without workspace), POD_ERR_HIP. */
 pod_status_t pod_attn_run(pod_attn_plan_t plan, const pod_attn_tensors_t* t,
@@ -337,7 +343,7 @@ pod_status_t pod_attn_run(pod_attn_plan_t plan, const pod_attn_tensors_t* t,
 /* pod_attn_run that also records two caller-created events on `stream`,
  * immediately before and after the fused kernel's launch (the merge kernel,
  * when any, follows `after_fused`), so that the fused kernel alone can be
- * timed.  Either event may be NULL (not recorded).  The work done is exactly
+ * timed; for a batch of one kind, around that one kernel.  Either event may be NULL (not recorded).  The work done is exactly
  * that of pod_attn_run.  Errors as pod_attn_run, plus POD_ERR_HIP when an
  * event cannot be recorded. */
 pod_status_t pod_attn_run_events(pod_attn_plan_t plan, const pod_attn_tensors_t* t,

@@ -138,7 +138,6 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   if (!pl->seq_is_fused)
     build_lists(pl->batch, dev, slots, kSeqPrefillHalfItemsPerSlot, slots * kWavesPerWG, kSeqDecodeUnitsPerWave,
                 t.prefill_kv_splits, t.decode_kv_splits, &pl->seq);
-  const WorkLists& sq = pl->seq_is_fused ? pl->fused : pl->seq;
   // Batched-prefill comparator: every request through the prefill kernel,
   // split like the sequential plan's prefill.
   pl->has_bp = (t.flags & POD_FLAG_BATCHED_PREFILL) != 0;
@@ -558,11 +557,52 @@ pod_status_t pod_attn_plan_scratch(const pod_attn_params_t* params, int32_t num_
                        decode_kv_len, tuning, ws, kScratchBytes, &need, stream, out_plan);
 }
 
+namespace {
+
+// Prefill kernel, decode kernel, merge on one stream with the sequential
+// plan's lists; `before` / `after` (may be NULL) are recorded around the
+// kernels that precede the merge.
+pod_status_t run_sequential(pod_attn_plan_t pl, const pod_attn_tensors_t* t, hipStream_t stream,
+                            hipEvent_t before, hipEvent_t after) {
+  const WorkLists& w = pl->seq_is_fused ? pl->fused : pl->seq;
+  KernelArgs a = make_args(pl, t, w, pl->dl_seq);
+  pick_counters(pl, kKindSeq, stream, &a);
+  // the trace is indexed by the fused lists' units, so only a plan-matched
+  // sequential run records it
+  if (pl->trace_records && pl->seq_is_fused)
+    a.trace = (pod_trace_record_t*)(pl->ws + pl->off_trace);
+  const int kvm = kv_mode_of(pl);
+  hipError_t e;
+  if (before && (e = hipEventRecord(before, stream)) != hipSuccess)
+    return hip_err(e, "hipEventRecord(before)");
+  if (w.n_p() > 0) {
+    e = launch_prefill(a, kvm, w.n_p(), stream);
+    if (e != hipSuccess) return hip_err(e, "prefill kernel launch");
+    if (!a.self_reset) ++pl->launches[kKindSeq];
+  }
+  if (w.n_groups() > 0) {
+    e = is_fp8(pl) ? launch_decode_fp8(a, kvm, w.n_groups(), stream)
+                   : launch_decode(a, kvm, w.n_groups(), stream);
+    if (e != hipSuccess) return hip_err(e, "decode kernel launch");
+  }
+  if (after && (e = hipEventRecord(after, stream)) != hipSuccess)
+    return hip_err(e, "hipEventRecord(after)");
+  return launch_merge_of(a, w, stream);
+}
+
+}  // namespace
+
 pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t,
                                  hipStream_t stream, hipEvent_t before_fused,
                                  hipEvent_t after_fused) {
   pod_status_t st = check_tensors(pl, t);
   if (st != POD_OK) return st;
+  // A batch of one kind (no decodes, or no prefill) has nothing to overlap:
+  // it runs the one kernel it needs with the sequential plan's lists, as the
+  // fused launch would only hold units of that kind.  (Traced plans keep the
+  // fused launch: the trace is indexed by its units.)
+  if (!pl->has_prefix && !pl->trace_records && (pl->fused.n_p() == 0 || pl->fused.n_d() == 0))
+    return run_sequential(pl, t, stream, before_fused, after_fused);
   const WorkLists& w = pl->fused;
   KernelArgs a = make_args(pl, t, w, pl->dl_fused);
   pick_counters(pl, kKindFused, stream, &a);
@@ -603,25 +643,7 @@ pod_status_t pod_attn_sequential_run(pod_attn_plan_t pl, const pod_attn_tensors_
                                      hipStream_t stream) {
   pod_status_t st = check_tensors(pl, t);
   if (st != POD_OK) return st;
-  const WorkLists& w = pl->seq_is_fused ? pl->fused : pl->seq;
-  KernelArgs a = make_args(pl, t, w, pl->dl_seq);
-  pick_counters(pl, kKindSeq, stream, &a);
-  // the trace is indexed by the fused lists' units, so only a plan-matched
-  // sequential run records it
-  if (pl->trace_records && pl->seq_is_fused)
-    a.trace = (pod_trace_record_t*)(pl->ws + pl->off_trace);
-  const int kvm = kv_mode_of(pl);
-  if (w.n_p() > 0) {
-    hipError_t e = launch_prefill(a, kvm, w.n_p(), stream);
-    if (e != hipSuccess) return hip_err(e, "prefill kernel launch");
-    if (!a.self_reset) ++pl->launches[kKindSeq];
-  }
-  if (w.n_groups() > 0) {
-    hipError_t e = is_fp8(pl) ? launch_decode_fp8(a, kvm, w.n_groups(), stream)
-                              : launch_decode(a, kvm, w.n_groups(), stream);
-    if (e != hipSuccess) return hip_err(e, "decode kernel launch");
-  }
-  return launch_merge_of(a, w, stream);
+  return run_sequential(pl, t, stream, nullptr, nullptr);
 }
 
 pod_status_t pod_attn_streams_run(pod_attn_plan_t pl, const pod_attn_tensors_t* t,
