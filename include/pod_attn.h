@@ -278,7 +278,8 @@ pod_status_t pod_attn_plan_host(const pod_attn_params_t* params,
  * member's own keys run as ordinary decode units; every (request, head)
  * result is merged by log-sum-exp.  pod_attn_plan_export lists the prefix
  * tiles as list 0 (in decode-item fields, up to 64 rows) and the suffix
- * units as list 1.
+ * units as list 1.  The trace and one-workgroup-per-unit flags are ignored
+ * (the packed kernel has one launch shape and records no trace).
  * pod_attn_run runs this packed path; pod_attn_sequential_run and
  * pod_attn_streams_run run the ordinary (unshared) decode of the same batch,
  * the baseline.  Workspace, ownership and errors as pod_attn_plan, plus

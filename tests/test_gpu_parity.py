@@ -260,3 +260,27 @@ def test_graph_replays_match_eager():
         eager = run_path(r, "fused")
         for k in ref:
             assert np.array_equal(eager[k], ref[k]), ("eager after replay", i, k)
+
+
+@pytest.mark.parametrize("which", [2, 3], ids=["only_prefill", "only_decode"])
+def test_single_kind_batch(which):
+    """A batch of one kind has nothing to overlap: pod_attn_run runs the one
+    kernel it needs with the sequential plan's lists (bitwise the sequential
+    result); a traced plan keeps the fused launch (its trace covers every
+    unit), and both match the oracle."""
+    spec = edge_specs()[which]
+    say(f"[single kind] {spec.name}")
+    b = inputs.make_batch_host(spec, poison=True)
+    ref = oracle.batch_attention(b)
+    r = B.BatchRunner(b)
+    f, s = run_path(r, "fused"), run_path(r, "seq")
+    compare(f, ref, f"{spec.name}/fused")
+    for k in f:
+        assert np.array_equal(f[k], s[k]), k
+    rt = B.BatchRunner(b, B.make_tuning(flags=B.FLAG_TRACE))
+    ft = run_path(rt, "fused")
+    compare(ft, ref, f"{spec.name}/fused traced")
+    tr = rt.plan.read_trace()
+    info = rt.plan.info()
+    assert len(tr) == info["trace_records"] == info["prefill_items"] + info["decode_items"] > 0
+    assert np.all(tr[:, 5] >= tr[:, 4]) and np.all(tr[:, 4] > 0)     # t_end >= t_start > 0
