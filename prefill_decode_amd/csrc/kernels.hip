@@ -1312,7 +1312,6 @@ __device__ __forceinline__ int claim_prefill(const KernelArgs& a, int xcc, int* 
     seen[i] = i < np ? peek(hot(a, CS_POOL + (xcc + i) % np)) : 0;
   const int oe = peek(hot(a, CS_EMPTY + 1));
   if (k0 < a.pool_off[p0 + 1] - a.pool_off[p0]) return a.pool_off[p0] + k0;
-#pragma unroll
   for (int i = 1; i < kMaxPools; ++i) {
     if (i >= np) break;
     const int p = (xcc + i) % np;
@@ -1339,7 +1338,6 @@ __device__ __forceinline__ int claim_prefill(const KernelArgs& a, int xcc, int* 
 __device__ __forceinline__ int claim_decode_others(const KernelArgs& a, int q0, const int* seen,
                                                    int oe, int* other_empty) {
   const int nq = a.n_dq, ng = a.n_groups;
-#pragma unroll
   for (int i = 1; i < kMaxDecodeQueues; ++i) {
     if (i >= nq) break;
     const int q = (q0 + i) % nq;
