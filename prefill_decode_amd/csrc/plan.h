@@ -51,9 +51,10 @@ constexpr int kSeqDecodeUnitsPerWave = 2;
 // tail, and the prefill need only finish beside it) and 3 per slot of the
 // whole GPU when it is large (its last items form the tail, and finer items
 // balance it).  Measured in interleaved runs: 1.5 against 2 per slot, 3.5%
-// faster on the llama3-8b layer; 3 against 2, 5% faster on the 70B layer
-// (against 1 or 4: 1%; the batched mix and the llama2-7b layer keep their
-// speed).  The sequential plan takes one item per slot.
+// faster on the llama3-8b layer; 3 against 2, 0.8% faster on the 70B layer,
+// and finer splits slower there (4: 1.5%, 6: 7%, 8: 10%), since each split
+// adds an fp32 partial whose traffic competes with the decode stream.  The
+// sequential plan takes one item per slot.
 constexpr int kFusedPrefillHalfItemsPerSlotSmall = 3;
 constexpr int kFusedPrefillHalfItemsPerSlotLarge = 6;
 constexpr int kSeqPrefillHalfItemsPerSlot = 2;
