@@ -168,9 +168,9 @@ def test_split_cap_two_waves():
     # [POD] "Cap prefill splitting": tiles x splits <= 2 x slots.  The
     # sequential list keeps that cap (it aims at one item per slot).  The
     # fused list departs from it for large prefills (> 1536 tokens): 3 items
-    # per slot of the whole GPU, three waves, which measured 5% faster on the
-    # 70B-shaped layer than two; small prefills aim at 1.5 items per slot of
-    # the prefill CUs.
+    # per slot of the whole GPU, three waves, which measured 0.8% faster on
+    # the 70B-shaped layer than two (more waves were slower); small prefills
+    # aim at 1.5 items per slot of the prefill CUs.
     slots = 256 * 2
     for spec in _specs():
         pl = _spec_lists(spec, match_sequential=0)
