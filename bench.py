@@ -733,8 +733,19 @@ def main():
             per[key] = f
             del r, _rest
             torch.cuda.empty_cache()
-        # decode-only batches with a bf16 and an FP8 E4M3 cache (the FP8
-        # path's scope): the decodes of the llama2-7b and 70B-shaped layers
+        # the hybrid layers with an FP8 E4M3 cache (fused FP8 kernel against
+        # the FP8 prefill and decode kernels run back to back)
+        for name in ("llama3_8b", "llama2_7b", "l70b_tp1", "batched"):
+            spec_f = inputs.fp8_spec(name)
+            print(f"bench: {spec_f.name}", file=sys.stderr, flush=True)
+            r, *_rest, f = measure_config(torch, B, inputs, metrics, timer, name, None,
+                                          args.config_steps, 2, tuning_kw,
+                                          paths=("fused", "seq", "streams"), spec=spec_f)
+            per[spec_f.name] = f
+            del r, _rest
+            torch.cuda.empty_cache()
+        # decode-only batches with a bf16 and an FP8 E4M3 cache: the decodes
+        # of the llama2-7b and 70B-shaped layers
         for name in ("llama2_7b", "l70b_tp1"):
             for dt in ("bf16", "fp8_e4m3"):
                 spec_d = inputs.decode_only_spec(name, dt)

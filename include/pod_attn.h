@@ -66,8 +66,11 @@ typedef enum { POD_KV_CONTIGUOUS = 0, POD_KV_PAGED = 1 } pod_kv_layout_t;
  * one fp32 scale per KV head for K and one for V (value = decoded byte times
  * its head's scale); a lever on decode's bytes named in "Prefill vs. Decode
  * GPU Utilization Imbalance", section "Quantization and compression as a
- * lever on both the bandwidth and capacity problem".  Supported for
- * decode-only batches with a contiguous cache or pages of >= 16 tokens. */
+ * lever on both the bandwidth and capacity problem".  Supported for every
+ * batch (prefill, decode or both) with a contiguous cache or pages of >= 16
+ * tokens; the prefill tile converts each staged K/V tile to 16-bit in LDS
+ * (K to bf16, V to fp16) and runs its PV product on fp16 P, the decode unit
+ * converts in registers. */
 typedef enum { POD_KV_BF16 = 0, POD_KV_FP8_E4M3 = 1 } pod_kv_dtype_t;
 
 /* Scheduler modes of the fused kernel: how the two workgroups of each CU
@@ -236,11 +239,11 @@ typedef struct {
  * different streams must not overlap: they share the workspace.
  * Errors: POD_ERR_INVALID_ARGUMENT (lengths, heads, scale, layout, dtype,
  * NULL length arrays with a nonzero count), POD_ERR_UNSUPPORTED (head_dim !=
- * 128, wgs_per_cu other than 0 or 2, an FP8 cache with prefill requests or
- * pages of fewer than 16 tokens), POD_ERR_WORKSPACE_TOO_SMALL, POD_ERR_HIP.
- * With an FP8 cache (decode-only) every run entry point runs the FP8 decode
- * kernel and the merge (there is no prefill to fuse with); the
- * batched-prefill comparator is not available. */
+ * 128, wgs_per_cu other than 0 or 2, an FP8 cache with pages of fewer than
+ * 16 tokens, or with the batched-prefill comparator),
+ * POD_ERR_WORKSPACE_TOO_SMALL, POD_ERR_HIP.  With an FP8 cache every run
+ * entry point runs the FP8 forms of its kernels (fused: the FP8 prefill tile
+ * beside the FP8 decode unit). */
 pod_status_t pod_attn_plan(const pod_attn_params_t* params,
                            int32_t num_prefill, const int32_t* prefill_qo_len,
                            const int32_t* prefill_kv_len,

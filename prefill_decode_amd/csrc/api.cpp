@@ -234,7 +234,8 @@ pod_status_t check_tensors(const pod_attn_plan_s* pl, const pod_attn_tensors_t* 
     if ((st = need(t->q_decode, "q_decode")) != POD_OK) return st;
     if ((st = need(t->o_decode, "o_decode")) != POD_OK) return st;
   }
-  if (pl->batch.params.kv_dtype == POD_KV_FP8_E4M3 && has_d && (!t->k_scale || !t->v_scale))
+  if (pl->batch.params.kv_dtype == POD_KV_FP8_E4M3 && (has_p || has_d) &&
+      (!t->k_scale || !t->v_scale))
     return set_err(POD_ERR_INVALID_ARGUMENT, "k_scale/v_scale is NULL (FP8 KV cache)");
   return POD_OK;
 }
@@ -283,6 +284,7 @@ KernelArgs make_args(const pod_attn_plan_s* pl, const pod_attn_tensors_t* t, con
   a.lse_decode = t->lse_decode;
   a.k_scale = t->k_scale;
   a.v_scale = t->v_scale;
+  a.kv_fp8 = p.kv_dtype == POD_KV_FP8_E4M3;
   a.d_members = (const int32_t*)(pl->ws + pl->off_members);
   a.pack_rpr = std::min(p.num_qo_heads / p.num_kv_heads, kDecodeRows);
   a.part_o = (float*)(pl->ws + pl->off_part_o);
@@ -620,11 +622,6 @@ pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t
     const int pgrid = w.n_p() + w.n_groups();
     if (pgrid > 0 && (e = launch_decode_pack(a, kv_mode_of(pl), pgrid, stream)) != hipSuccess)
       return hip_err(e, "packed decode kernel launch");
-  } else if (is_fp8(pl)) {
-    // decode-only FP8 batch: nothing to fuse with; the FP8 decode kernel
-    if (w.n_groups() > 0 && (e = launch_decode_fp8(a, kv_mode_of(pl), w.n_groups(), stream)) !=
-                                hipSuccess)
-      return hip_err(e, "FP8 decode kernel launch");
   } else if (grid > 0) {
     e = launch_fused(a, kv_mode_of(pl), grid, stream);
     if (e != hipSuccess) return hip_err(e, "fused kernel launch");

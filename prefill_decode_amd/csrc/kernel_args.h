@@ -81,6 +81,7 @@ struct KernelArgs {
   float merge_lse_scale;  // factor taking part_lse to log2 (1, or log2(e) for natural log)
   const float* k_scale;   // FP8 KV: per-KV-head scales (device fp32 [Hkv])
   const float* v_scale;
+  int32_t kv_fp8;         // 1: K and V are FP8 E4M3 (the F8 kernels)
   const int32_t* d_members;  // shared-prefix plans: decode index of each group member
   int32_t pack_rpr;          // shared-prefix plans: tile rows per member (min(g, 16))
 };

@@ -59,6 +59,8 @@ constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kRowBytes = kHeadDim * 2;                      // 256
 constexpr int kTileBytes = kPrefillKeys * kRowBytes;         // 16384
 constexpr int kDecStepBytes = kDecodeStep * kRowBytes;       // 8192
+constexpr int kRow8 = kHeadDim;                              // FP8 row: 128 bytes
+constexpr int kTile8 = kPrefillKeys * kRow8;                 // 8192
 // A workgroup owns two LDS objects of 32 KiB (64 KiB in all, so two
 // workgroups fit a CU's 160 KiB): X = {K tile 0, V tile 0}, Y = {K tile 1,
 // V tile 1}.  Prefill iteration t reads the tiles of parity t & 1 while the
@@ -77,6 +79,8 @@ __device__ __forceinline__ int kswz(int r) { return r & 15; }
 __device__ __forceinline__ int vswz(int r) { return (int)((kVSwz >> (4 * (r & 7))) & 15u); }
 
 __device__ __forceinline__ bf16x8 as_bf(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16x8 as_f16(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ float fmax_(float a, float b) { return __builtin_fmaxf(a, b); }
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -114,6 +118,13 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 r;
+  r[0] = (_Float16)lo;
+  r[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 r;
@@ -155,6 +166,22 @@ __device__ __forceinline__ u32x2 tr_read(const char* p) {
   const v4s t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) v4s*)(const_cast<char*>(p)));
   return __builtin_bit_cast(u32x2, t);
+}
+
+// eight E4M3 bytes (two dwords, byte order = element order) to eight bf16
+// (exact: E4M3 values are bf16 values)
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+#define POD_CVT(w, upper) \
+  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, upper))
+  return u32x4{POD_CVT(lo, false), POD_CVT(lo, true), POD_CVT(hi, false), POD_CVT(hi, true)};
+#undef POD_CVT
+}
+// the same to eight fp16 (exact: E4M3 values are fp16 values)
+__device__ __forceinline__ u32x4 fp8x8_to_f16(uint32_t lo, uint32_t hi) {
+#define POD_CVT(w, upper) \
+  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, upper))
+  return u32x4{POD_CVT(lo, false), POD_CVT(lo, true), POD_CVT(hi, false), POD_CVT(hi, true)};
+#undef POD_CVT
 }
 
 // ---------------------------------------------------------------------------
@@ -208,8 +235,18 @@ struct KvAddr {
 // a decode request (index >= n_preq) read their query row from q_decode and
 // write o_decode / lse_decode, i.e. a decode runs through this tile as a
 // one-row chunk.
+//
+// F8 (FP8 E4M3 KV cache, per-KV-head scales): a tile's FP8 K and V rows
+// (128 bytes) are staged by LDS DMA into object Y, then the workgroup
+// converts them, once for all its waves, into the 16-bit tiles of object X in
+// the layout above (K to bf16; V to fp16, exact like bf16), and the halves
+// run on X as for bf16, except that P is rounded to fp16 and PV is an fp16
+// MFMA: two more mantissa bits for P at the same rate.  The next tile's DMA
+// is issued after the conversion (so it never waits on the reads of Y) and
+// lands while X is computed.  The K scale multiplies the score with sm_scale,
+// the V scale the output.
 // ---------------------------------------------------------------------------
-template <int KVM, bool BP = false>
+template <int KVM, bool BP = false, bool F8 = false>
 __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char* __restrict__ kt0,
                                              char* __restrict__ kt1, char* __restrict__ vt0,
                                              char* __restrict__ vt1) {
@@ -232,16 +269,20 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   const int wpos = kWaveRows * (wave - hidx * wph);  // first position (item-relative)
   const int head = head0 + hidx;
   const int kvh = head0 / a.group;
-  const uint32_t tok = (uint32_t)a.hkv * kRowBytes;
-  const char* kbase = (const char*)a.k + kvh * kRowBytes;
-  const char* vbase = (const char*)a.v + kvh * kRowBytes;
+  constexpr int kSrcRow = F8 ? kRow8 : kRowBytes;     // bytes of one head's K or V row
+  const uint32_t tok = (uint32_t)a.hkv * kSrcRow;
+  const char* kbase = (const char*)a.k + kvh * kSrcRow;
+  const char* vbase = (const char*)a.v + kvh * kSrcRow;
   KvAddr<KVM> addr;
   addr.init(a, kvreq);
   const int span = kv_end - kv_begin;
   const int ntiles = (span + kPrefillKeys - 1) / kPrefillKeys;
   const int nfull = span / kPrefillKeys;
   const bool causal = a.causal != 0;
-  const float sl2 = a.scale_log2;
+  // FP8: the KV head's scales (uniform, through the scalar cache)
+  const float sl2 = F8 ? a.scale_log2 * __builtin_bit_cast(float, ((cptr)a.k_scale)[kvh])
+                       : a.scale_log2;
+  const float vsc = F8 ? __builtin_bit_cast(float, ((cptr)a.v_scale)[kvh]) : 1.0f;
   // keys this wave needs: tiles [0, t_act); tiles >= t_mask need masking
   const int nvalid = min(kWaveRows, nrows - wpos);  // may be <= 0
   const int pos_lo = pos0 + wpos;
@@ -422,7 +463,9 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p[ks][e] = pack_bf16x2(sx[8 * ks + 2 * e], sx[8 * ks + 2 * e + 1]);
+      for (int e = 0; e < 4; ++e)
+        p[ks][e] = F8 ? pack_f16x2(sx[8 * ks + 2 * e], sx[8 * ks + 2 * e + 1])
+                      : pack_bf16x2(sx[8 * ks + 2 * e], sx[8 * ks + 2 * e + 1]);
   };
   // O^T += V^T P^T for one 32-key half: one V^T operand (two transposing
   // reads), two MFMAs; operand reads one ahead and DMAs placed as in qk
@@ -440,9 +483,14 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
     for (int i = 0; i < 8; ++i) {
       const int ks = i >> 2, db = i & 3;
       const u32x4 vnext = i < 7 ? vop(i + 1) : vcur;
-      oa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vcur), as_bf(pa[ks]), oa[db], 0, 0, 0);
-      if (i & 1) dma(i >> 1);
-      ob[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vcur), as_bf(pb[ks]), ob[db], 0, 0, 0);
+      if constexpr (F8) {
+        oa[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16(vcur), as_f16(pa[ks]), oa[db], 0, 0, 0);
+        ob[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16(vcur), as_f16(pb[ks]), ob[db], 0, 0, 0);
+      } else {
+        oa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vcur), as_bf(pa[ks]), oa[db], 0, 0, 0);
+        if (i & 1) dma(i >> 1);
+        ob[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vcur), as_bf(pb[ks]), ob[db], 0, 0, 0);
+      }
       vcur = vnext;
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -489,8 +537,10 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
   // iteration t: K(t) and V(t) are in LDS buffers t&1; DMA of tile t+1
   // goes to the other buffers, which the barrier released
   __amdgpu_buffer_rsrc_t rk = block_rsrc(0, kbase), rv = block_rsrc(0, vbase);
-  stage(0, true, 0, rk);
-  stage(0, false, 0, rv);
+  if constexpr (!F8) {
+    stage(0, true, 0, rk);
+    stage(0, false, 0, rv);
+  }
   // DMA of row group i (rows 4i .. 4i + 3 of this wave's 16) of tile t into
   // buffers `buf`, without branches, so that it can sit among a half's
   // MFMAs: rows past the last key read as zeros (the block's resource ends
@@ -547,16 +597,66 @@ __device__ __forceinline__ void prefill_tile(const KernelArgs& a, cptr it, char*
       if (h1) half(t, 1, kb, vb, masked, nothing, nothing);
     }
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    body(t, std::integral_constant<int, 0>{});
-    if (t + 1 < ntiles) body(t + 1, std::integral_constant<int, 1>{});
+  if constexpr (F8) {
+    // stage: this wave's 16 rows of tile t, eight 128-byte rows per DMA
+    // (lane L: row L / 8, chunk L % 8), into Y's K and V staging tiles;
+    // rows past the last key read as zeros (bounded block resource)
+    char* const k8 = kt1;
+    char* const v8 = vt1;
+    auto stage8 = [&](int t) {
+      int sl = threadIdx.x;
+      asm volatile("" : "+v"(sl));
+      const uint32_t vo = (uint32_t)((sl >> 3) & 7) * tok + 16u * (uint32_t)(sl & 7);
+      const __amdgpu_buffer_rsrc_t r8k = block_rsrc(t, kbase), r8v = block_rsrc(t, vbase);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        dma16(r8k, k8 + (16 * wave + 8 * i) * kRow8, vo + 8u * i * tok, 0);
+        dma16(r8v, v8 + (16 * wave + 8 * i) * kRow8, vo + 8u * i * tok, 0);
+      }
+    };
+    // convert: bf16 chunk c = tid + 256 j of each tile (row c / 16, chunk
+    // c % 16) from the staged row's bytes 8 (c % 16) .. + 7, stored at the
+    // swizzled chunk position the halves read
+    auto convert8 = [&]() {
+      int sl = threadIdx.x;
+      asm volatile("" : "+v"(sl));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = sl + 256 * j;
+        const int r = c >> 4, ch = c & 15;
+        const u32x2 kb8 = *(const u32x2*)(k8 + r * kRow8 + 8 * ch);
+        const u32x2 vb8 = *(const u32x2*)(v8 + r * kRow8 + 8 * ch);
+        *(u32x4*)(kt0 + r * kRowBytes + 16 * (ch ^ kswz(r))) = fp8x8_to_bf16(kb8[0], kb8[1]);
+        *(u32x4*)(vt0 + r * kRowBytes + 16 * (ch ^ vswz(r))) = fp8x8_to_f16(vb8[0], vb8[1]);
+      }
+    };
+    stage8(0);
+    for (int t = 0; t < ntiles; ++t) {
+      wait_vmem<0>();
+      __syncthreads();                     // tile t staged in Y; X free
+      convert8();
+      __syncthreads();                     // X holds tile t; Y free
+      if (t + 1 < ntiles) stage8(t + 1);
+      if (t < t_act) {
+        const int k1 = kv_begin + t * kPrefillKeys + 32;
+        const bool h1 = k1 < kv_end && (!causal || k1 <= pos_hi);
+        const bool masked = t >= t_mask;
+        half(t, 0, kt0, vt0, masked, nothing, nothing);
+        if (h1) half(t, 1, kt0, vt0, masked, nothing, nothing);
+      }
+    }
+  } else {
+    for (int t = 0; t < ntiles; t += 2) {
+      body(t, std::integral_constant<int, 0>{});
+      if (t + 1 < ntiles) body(t + 1, std::integral_constant<int, 1>{});
+    }
   }
 
   // epilogue: lanes l and l^32 hold the same query row of a block
   auto finish = [&](const f32x16 (&o)[4], float m, float l, bool ok, int r) {
     const float l_tot = sum_x32(l);
     if (!ok) return;
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float inv = l_tot > 0.0f ? vsc / l_tot : 0.0f;
     const float lse2 = l_tot > 0.0f ? m + log2_(l_tot) : kNegInf;
     if (part < 0) {
       uint16_t* const o_dst = dec_item ? a.o_decode : a.o_prefill;
@@ -1066,14 +1166,6 @@ __device__ __forceinline__ void prefix_tile(const KernelArgs& a, cptr it, char* 
 //      multiplies the final O.
 // A step's raw K and V of the next step are in flight while it computes.
 // ---------------------------------------------------------------------------
-// eight E4M3 bytes (two dwords, byte order = element order) to eight bf16
-// (exact: E4M3 values are bf16 values)
-__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
-#define POD_CVT(w, upper) \
-  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, upper))
-  return u32x4{POD_CVT(lo, false), POD_CVT(lo, true), POD_CVT(hi, false), POD_CVT(hi, true)};
-#undef POD_CVT
-}
 
 template <int KVM>
 __device__ __forceinline__ void decode_unit_fp8(const KernelArgs& a, cptr it, char* __restrict__ vbuf) {
@@ -1449,8 +1541,9 @@ __device__ __forceinline__ void trace_unit(const KernelArgs& a, int rec, int rol
 // counter (prefill for its share of the CU's slots), and works through the
 // queue of that role: prefill tiles one workgroup at a time, decode units in
 // groups of four (one per wave).  When its queue runs dry it moves to the
-// other queue, so no slot idles while work is left.
-template <int KVM, bool ONE = false>
+// other queue, so no slot idles while work is left.  F8: an FP8 KV cache
+// (the prefill tile's F8 form and the FP8 decode unit).
+template <int KVM, bool ONE = false, bool F8 = false>
 __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
   POD_LDS_OBJECTS
   const int tid = threadIdx.x;
@@ -1498,7 +1591,7 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
       const int u = rfl(s_info[2]);
       if (u < 0) return rfl(s_info[3]) != 0;
       const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
-      prefill_tile<KVM>(a, (cptr)a.p_items + u * P_FIELDS, POD_PREFILL_BUFFERS);
+      prefill_tile<KVM, false, F8>(a, (cptr)a.p_items + u * P_FIELDS, POD_PREFILL_BUFFERS);
       if (a.trace && tid == 0) trace_unit(a, u, 0, u, slot, t0);
     }
   };
@@ -1528,8 +1621,11 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
       int ticket = -1;
       if (u < a.n_d) {
         const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
-        decode_unit<KVM>(a, (cptr)a.d_items + u * D_FIELDS, db0, db1,
-                         wave == 0 ? hot(a, CS_DQ + q0) : nullptr, ticket);
+        if constexpr (F8)
+          decode_unit_fp8<KVM>(a, (cptr)a.d_items + u * D_FIELDS, db0);
+        else
+          decode_unit<KVM>(a, (cptr)a.d_items + u * D_FIELDS, db0, db1,
+                           wave == 0 ? hot(a, CS_DQ + q0) : nullptr, ticket);
         if (a.trace && lane == 0) trace_unit(a, a.n_p + u, 1, u, slot, t0);
       }
       pair = 7 - pair;
@@ -1558,15 +1654,19 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
     const int u = rfl(s_info[2]), g = rfl(s_info[3]);
     if (u >= 0) {
       const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
-      prefill_tile<KVM>(a, (cptr)a.p_items + u * P_FIELDS, POD_PREFILL_BUFFERS);
+      prefill_tile<KVM, false, F8>(a, (cptr)a.p_items + u * P_FIELDS, POD_PREFILL_BUFFERS);
       if (a.trace && tid == 0) trace_unit(a, u, 0, u, slot, t0);
     } else if (g >= 0) {
       POD_DECODE_BUFFERS(wave)
       const int du = g * kWavesPerWG + wave;
       if (du < a.n_d) {
         const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
-        int ticket;
-        decode_unit<KVM>(a, (cptr)a.d_items + du * D_FIELDS, db0, db1, nullptr, ticket);
+        if constexpr (F8) {
+          decode_unit_fp8<KVM>(a, (cptr)a.d_items + du * D_FIELDS, db0);
+        } else {
+          int ticket;
+          decode_unit<KVM>(a, (cptr)a.d_items + du * D_FIELDS, db0, db1, nullptr, ticket);
+        }
         if (a.trace && lane == 0) trace_unit(a, a.n_p + du, 1, du, slot, t0);
       }
     }
@@ -1581,7 +1681,7 @@ __global__ __launch_bounds__(256, 2) void pod_fused_kernel(KernelArgs a) {
   }
 }
 
-template <int KVM, bool BP = false>
+template <int KVM, bool BP = false, bool F8 = false>
 __global__ __launch_bounds__(256, 2) void pod_prefill_kernel(KernelArgs a) {
   POD_LDS_OBJECTS
   zero_next_counters(a);
@@ -1594,7 +1694,7 @@ __global__ __launch_bounds__(256, 2) void pod_prefill_kernel(KernelArgs a) {
   __syncthreads();
   if (unit >= 0) {
     const uint64_t t0 = a.trace ? __builtin_amdgcn_s_memrealtime() : 0;
-    prefill_tile<KVM, BP>(a, (cptr)a.p_items + rfl(unit) * P_FIELDS, POD_PREFILL_BUFFERS);
+    prefill_tile<KVM, BP, F8>(a, (cptr)a.p_items + rfl(unit) * P_FIELDS, POD_PREFILL_BUFFERS);
     if (a.trace && threadIdx.x == 0) trace_unit(a, unit, 0, unit, cu_slot_id(), t0);
   }
   finish_launch(a, &s_info[1]);
@@ -1822,14 +1922,16 @@ hipError_t scratch_address(int device, void** out) {
   }                                                                                      \
   return hipGetLastError();
 
-template <bool ONE>
+template <bool ONE, bool F8>
 struct FusedK {
   template <int KVM>
   static void launch(int grid, hipStream_t s, const KernelArgs& a) {
-    hipLaunchKernelGGL((pod_fused_kernel<KVM, ONE>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pod_fused_kernel<KVM, ONE, F8>), dim3(grid), dim3(256), 0, s, a);
   }
 };
 
+// FP8 caches have pages of at least 16 tokens (or are contiguous), so the
+// narrow-page form is not instantiated for them.
 hipError_t launch_fused(const KernelArgs& a, int kv_mode, int grid, hipStream_t s) {
   auto go = [&](auto k) {
     using K = decltype(k);
@@ -1839,16 +1941,28 @@ hipError_t launch_fused(const KernelArgs& a, int kv_mode, int grid, hipStream_t 
       default: K::template launch<KV_PAGED_NARROW>(grid, s, a); break;
     }
   };
-  if (a.one_unit) go(FusedK<true>{});
-  else go(FusedK<false>{});
+  auto go8 = [&](auto k) {
+    using K = decltype(k);
+    if (kv_mode == KV_CONTIG) K::template launch<KV_CONTIG>(grid, s, a);
+    else K::template launch<KV_PAGED_WIDE>(grid, s, a);
+  };
+  if (a.kv_fp8) {
+    if (kv_mode == KV_PAGED_NARROW) return hipErrorInvalidValue;
+    if (a.one_unit) go8(FusedK<true, true>{});
+    else go8(FusedK<false, true>{});
+  } else if (a.one_unit) {
+    go(FusedK<true, false>{});
+  } else {
+    go(FusedK<false, false>{});
+  }
   return hipGetLastError();
 }
 
-template <bool BP>
+template <bool BP, bool F8>
 struct PrefillK {
   template <int KVM>
   static void launch(int grid, hipStream_t s, const KernelArgs& a) {
-    hipLaunchKernelGGL((pod_prefill_kernel<KVM, BP>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pod_prefill_kernel<KVM, BP, F8>), dim3(grid), dim3(256), 0, s, a);
   }
 };
 
@@ -1861,8 +1975,16 @@ hipError_t launch_prefill(const KernelArgs& a, int kv_mode, int grid, hipStream_
       default: K::template launch<KV_PAGED_NARROW>(grid, s, a); break;
     }
   };
-  if (batched) go(PrefillK<true>{});
-  else go(PrefillK<false>{});
+  if (a.kv_fp8) {
+    // FP8: no narrow pages, no batched-prefill comparator (both refused by the planner)
+    if (kv_mode == KV_PAGED_NARROW || batched) return hipErrorInvalidValue;
+    if (kv_mode == KV_CONTIG) PrefillK<false, true>::launch<KV_CONTIG>(grid, s, a);
+    else PrefillK<false, true>::launch<KV_PAGED_WIDE>(grid, s, a);
+  } else if (batched) {
+    go(PrefillK<true, false>{});
+  } else {
+    go(PrefillK<false, false>{});
+  }
   return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ Conventions: request order is all prefill requests, then all decodes;
 ``uniform in [a, b]`` is integers with both ends included; Q/K/V values are
 i.i.d. N(0, 1) drawn in float32 and rounded to bfloat16 (nearest-even).
 
-FP8 KV caches (``kv_dtype="fp8_e4m3"``, decode-only batches): K and V are
+FP8 KV caches (``kv_dtype="fp8_e4m3"``, any batch): K and V are
 drawn the same way in float32, each KV head gets the scale max|x| / 448 over
 its pool (float32), and the cache holds x / scale encoded as OCP FP8 E4M3
 (nearest, ties to even) -- so that the largest value of a head is the format's
@@ -138,9 +138,15 @@ def config_spec(name: str, n_dec: Optional[int] = None) -> BatchSpec:
     raise ValueError(f"unknown config {name!r}")
 
 
+def fp8_spec(name: str) -> BatchSpec:
+    """Workload ``name`` with an FP8 E4M3 KV cache (same lengths and seed)."""
+    base = config_spec(name)
+    return replace(base, name=base.name + "_fp8", kv_dtype="fp8_e4m3")
+
+
 def decode_only_spec(name: str, kv_dtype: str = "bf16") -> BatchSpec:
     """The decodes of workload ``name`` alone (its prefill dropped), with a
-    bf16 or an FP8 E4M3 cache (the FP8 path's scope is decode-only)."""
+    bf16 or an FP8 E4M3 cache."""
     base = config_spec(name)
     suffix = "_dec_fp8" if kv_dtype == "fp8_e4m3" else "_dec_bf16"
     return replace(base, name=base.name + suffix, prefill_qo_len=(), prefill_kv_len=(),

@@ -68,9 +68,10 @@ OK, INV, UNS = 0, 1, 2
     (dict(causal=2), INV),
     (dict(qo=[3], kv=[1 << 25], dkv=[]), UNS),
     (dict(kv_dtype=2), INV),                                # unknown dtype
-    (dict(kv_dtype=1), UNS),                                # FP8 cache with a prefill
+    (dict(kv_dtype=1), OK),                                 # FP8 cache, hybrid batch
     (dict(kv_dtype=1, qo=[], kv=[]), OK),                   # FP8 decode-only
     (dict(kv_dtype=1, qo=[], kv=[], page_size=8), UNS),     # FP8 needs pages >= 16
+    (dict(kv_dtype=1, page_size=8), UNS),                   # (also with a prefill)
 ])
 def test_plan_validation(case, expect):
     p = B.make_params(case.get("hq", 8), case.get("hkv", 2), "paged",
