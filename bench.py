@@ -66,6 +66,8 @@ DESCR = {
                    "groups of 8 sharing a 2048-token prefix + own U[64,1024]; paged 16; "
                    "fused = packed (PAT-style), sequential = unshared decode",
 }
+for _n in ("llama3_8b", "llama2_7b", "l70b_tp1", "batched"):
+    DESCR[_n + "_fp8"] = DESCR[_n] + "; FP8 E4M3 KV, per-head scales"
 COPY_BYTES = 1 << 30          # calibration copy for the HBM byte counters
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -88,10 +90,8 @@ def main_kernel(spec):
     batch of one kind runs the one kernel it needs."""
     if spec.prefix_groups:
         return "pod_decode_pack_kernel"
-    if spec.kv_dtype == "fp8_e4m3":
-        return "pod_decode_fp8_kernel"
     if not spec.prefill_qo_len:
-        return "pod_decode_kernel"
+        return "pod_decode_fp8_kernel" if spec.kv_dtype == "fp8_e4m3" else "pod_decode_kernel"
     if not spec.decode_kv_len:
         return "pod_prefill_kernel"
     return "pod_fused_kernel"
@@ -536,6 +536,9 @@ def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup,
         # decode on the sequential and streams paths; it has no batched or
         # ordered variant
         paths = tuple(p for p in paths if p in ("fused", "seq", "streams"))
+    if spec.kv_dtype == "fp8_e4m3":
+        # the batched-prefill comparator reads bf16 caches only
+        paths = tuple(p for p in paths if p != "batched")
     batch = inputs.make_batch_device(spec)
     counts = metrics.algorithmic_counts(spec)
     flags = B.FLAG_BATCHED_PREFILL if "batched" in paths else 0

@@ -100,7 +100,11 @@ CONFIG_NAMES = ("tiny", "llama3_8b", "llama2_7b", "l70b_tp1", "batched")
 def config_spec(name: str, n_dec: Optional[int] = None) -> BatchSpec:
     """The five workload shapes (module docstring), lengths drawn from their
     seeds.  ``n_dec`` (``batched`` only) selects a point of the decode-count
-    sweep."""
+    sweep.  A name ending in ``_fp8`` gives that workload with an FP8 E4M3
+    cache."""
+    if name.endswith("_fp8"):
+        base = config_spec(name[:-4], n_dec)
+        return replace(base, name=base.name + "_fp8", kv_dtype="fp8_e4m3")
     if name == "tiny":
         return BatchSpec(name, 8, 8, (128,), (384,), (512,) * 4,
                          layout="contiguous", seed=1234, extra_pages=0)
@@ -140,8 +144,7 @@ def config_spec(name: str, n_dec: Optional[int] = None) -> BatchSpec:
 
 def fp8_spec(name: str) -> BatchSpec:
     """Workload ``name`` with an FP8 E4M3 KV cache (same lengths and seed)."""
-    base = config_spec(name)
-    return replace(base, name=base.name + "_fp8", kv_dtype="fp8_e4m3")
+    return config_spec(name + "_fp8")
 
 
 def decode_only_spec(name: str, kv_dtype: str = "bf16") -> BatchSpec:
