@@ -209,3 +209,23 @@ def test_fp8_hybrid_fullsize_sampled(name):
             assert np.all(np.isfinite(got[k])), (spec.name, path, k)
     del runner, bd
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["l70b_tp1", "batched"])
+def test_fp8_hybrid_fullsize_every_row(name):
+    # every prefill row and decode of the full-size FP8 layer, fused and
+    # sequential, against the oracle of the whole batch
+    import torch
+    spec = inputs.fp8_spec(name)
+    say(f"[fp8-fullsize-all] {spec.name}: generating on device")
+    bd = inputs.make_batch_device(spec, poison=True)
+    runner = B.BatchRunner(bd)
+    host = inputs.host_subset(bd, list(range(spec.num_prefill)), list(range(spec.num_decode)))
+    say("  oracle on the whole batch")
+    ref = oracle.batch_attention(host)
+    del host
+    for path in ("fused", "seq"):
+        say(f"  path {path}")
+        compare(run_path(runner, path), ref, f"{spec.name}-all/{path}")
+    del runner, bd
+    torch.cuda.empty_cache()
