@@ -200,8 +200,15 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
         1, (std::max(1, p_half_items_per_slot) * prefill_slots) / (2 * (int64_t)tiles.size()));
     s_all = std::min(s_all, kMaxPrefillSplits);
   }
-  struct PI { std::vector<int32_t> f; double work; };
+  struct PI { std::array<int32_t, P_FIELDS> f; double work; };
   std::vector<PI> pitems;
+  {
+    // room for every merge task (at most one per prefill row and head, one
+    // per decode and head), so that filling the lists never reallocates
+    int64_t rows = 0;
+    for (int32_t x : b.qo) rows += x;
+    w.m_tasks.reserve((size_t)M_FIELDS * (size_t)((rows + nd) * hq));
+  }
   for (const Tile& t : tiles) {
     const int32_t n_kt = (int32_t)ceil_div(t.kv_end, kPrefillKeys);
     int32_t s = std::max(1, std::min(s_all, n_kt));
@@ -212,12 +219,16 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
     if (s > 1) {
       base = n_partials;
       n_partials += s * kPrefillRows;
+      const size_t at = w.m_tasks.size();
+      w.m_tasks.resize(at + (size_t)M_FIELDS * nh * t.nrows);
+      int32_t* q = w.m_tasks.data() + at;
+      const int32_t flags = s | (dec_tile ? 1 << 16 : 0);
       for (int32_t j = 0; j < nh; ++j)
-        for (int32_t i = 0; i < t.nrows; ++i) {
-          w.m_tasks.push_back((t.qrow0 + i) * hq + t.head + j);
-          w.m_tasks.push_back(base + j * npos + i);
-          w.m_tasks.push_back(kPrefillRows);
-          w.m_tasks.push_back(s | (dec_tile ? 1 << 16 : 0));
+        for (int32_t i = 0; i < t.nrows; ++i, q += M_FIELDS) {
+          q[0] = (t.qrow0 + i) * hq + t.head + j;
+          q[1] = base + j * npos + i;
+          q[2] = kPrefillRows;
+          q[3] = flags;
         }
     }
     w.p_splits_max = std::max(w.p_splits_max, s);
@@ -227,6 +238,7 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
       PI it;
       it.f = {t.qrow0, t.head, t.nrows, t.pos0, kb, ke, t.req,
               base < 0 ? -1 : base + k * kPrefillRows};
+      static_assert(P_FIELDS == 8, "prefill item fields");
       // a wave computes its 64 rows whatever the valid count, so a one-row
       // decode tile costs a full wave per head (batched prefill only; the
       // tuned lists keep the valid-row estimate)
@@ -261,6 +273,7 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
   for (int32_t x = 0; x < nx; ++x)
     std::stable_sort(pitems.begin() + w.pool_off[x], pitems.begin() + w.pool_off[x + 1],
                      [](const PI& a, const PI& c) { return a.work > c.work; });
+  w.p_items.reserve(pitems.size() * P_FIELDS);
   for (auto& it : pitems) w.p_items.insert(w.p_items.end(), it.f.begin(), it.f.end());
 
   // ---- decode units (request, KV head, <=16 query heads, split) ----
@@ -316,6 +329,7 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
   // shortest (and the four waves of a sequential decode workgroup get similar work)
   std::stable_sort(ditems.begin(), ditems.end(),
                    [](const DI& a, const DI& c) { return a.work > c.work; });
+  w.d_items.reserve(ditems.size() * D_FIELDS);
   for (auto& it : ditems) w.d_items.insert(w.d_items.end(), it.f.begin(), it.f.end());
   w.n_partials = n_partials;
   *out = std::move(w);
