@@ -431,7 +431,7 @@ Commands (from the repository root; `$D` = a scratch directory):
     print(txt)
 
 
-PATHS = ("fused", "seq", "streams", "batched", "ordered")
+PATHS = ("fused", "seq", "streams", "batched", "ordered", "graph")
 PATH_NAMES = {
     "fused": "pod_attn_run: one fused launch (+ merge)",
     "seq": "pod_attn_sequential_run: prefill kernel, decode kernel, merge on one stream",
@@ -440,6 +440,8 @@ PATH_NAMES = {
                "(decodes as one-row chunks), merge",
     "ordered": "pod_attn_run with the ordered scheduler: one persistent launch over a unified "
                "queue, prefill units first",
+    "graph": "pod_attn_run captured once into a HIP graph and replayed (the fused kernel's "
+             "self-resetting counters; no launch overhead per kernel)",
 }
 
 
@@ -574,6 +576,16 @@ def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup,
     if "ordered" in paths:
         ordered = B.BatchRunner(batch, B.make_tuning(sched_mode=B.SCHED_ORDERED))
         calls["ordered"] = ordered.run
+    graph = None
+    if "graph" in paths and spec.prefill_qo_len and spec.decode_kv_len and not spec.prefix_groups:
+        # the fused step captured once (hybrid batches: the fused launch + merge)
+        runner.run()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            runner.run()
+        torch.cuda.synchronize()
+        calls["graph"] = graph.replay
     t = timer.interleaved(calls, steps, warmup)
     # the fused kernel alone, as many launches again: events that
     # pod_attn_run_events records immediately around it (recorded inside the
@@ -593,7 +605,8 @@ def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup,
         "sequential_us": med["seq"] * 1e6,
         "sequential_us_p10_p90": [pct(t["seq"], 10), pct(t["seq"], 90)],
         "speedup_vs_sequential": med["seq"] / t_step,
-        "comparators_us": {k: med[k] * 1e6 for k in ("streams", "batched", "ordered") if k in med},
+        "comparators_us": {k: med[k] * 1e6 for k in ("streams", "batched", "ordered", "graph")
+                           if k in med},
         "overlap_roofline_us": roof_s * 1e6,
         "overlap_roofline_frac_step": roof_s / t_step,
         "overlap_roofline_frac_kernel": roof_s / t_kern,
@@ -608,7 +621,7 @@ def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup,
                  "prefill_quarters_per_cu": info["prefill_quarters_per_cu"],
                  "sched_mode": info["sched_mode"]},
     }
-    del ordered
+    del ordered, graph
     return runner, batch, spec, counts, t, kern, f
 
 
