@@ -187,9 +187,9 @@ def cpu_baseline(batch_dev, spec, budget_s=15.0):
 
 
 def pmc_run(args):
-    """Driver for `rocprofv3 --pmc` runs: a few fused runs, as many sequential
-    runs, and one plain 1 GiB device-to-device copy whose counters calibrate
-    the byte counters."""
+    """Driver for `rocprofv3 --pmc` runs: a few fused runs (the fused launch
+    even where the plan would run the two kernels back to back), as many
+    sequential runs, and one plain 1 GiB device-to-device copy."""
     import torch
 
     from prefill_decode_amd import binding as B
@@ -197,7 +197,11 @@ def pmc_run(args):
 
     torch.cuda.set_device(0)
     spec = inputs.config_spec(args.config, n_dec=args.n_dec)
-    runner = B.BatchRunner(inputs.make_batch_device(spec))
+    batch = inputs.make_batch_device(spec)
+    runner = B.BatchRunner(batch)
+    if runner.plan.info()["runs_sequential"]:
+        # the plan runs the two kernels back to back: count the fused launch itself
+        runner = B.BatchRunner(batch, B.make_tuning(sched_mode=B.SCHED_SPLIT))
     for _ in range(args.steps):
         runner.run()
     for _ in range(args.steps):
@@ -442,6 +446,8 @@ PATH_NAMES = {
                "queue, prefill units first",
     "graph": "pod_attn_run captured once into a HIP graph and replayed (the fused kernel's "
              "self-resetting counters; no launch overhead per kernel)",
+    "fused_launch": "where the plan runs the two kernels back to back (plan.runs_sequential), "
+                    "the fused launch itself (an explicit scheduler mode)",
 }
 
 
@@ -576,6 +582,10 @@ def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup,
     if "ordered" in paths:
         ordered = B.BatchRunner(batch, B.make_tuning(sched_mode=B.SCHED_ORDERED))
         calls["ordered"] = ordered.run
+    forced = None
+    if runner.plan.info()["runs_sequential"]:
+        forced = B.BatchRunner(batch, B.make_tuning(sched_mode=B.SCHED_SPLIT))
+        calls["fused_launch"] = forced.run
     graph = None
     if "graph" in paths and spec.prefill_qo_len and spec.decode_kv_len and not spec.prefix_groups:
         # the fused step captured once (hybrid batches: the fused launch + merge)
@@ -605,8 +615,8 @@ def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup,
         "sequential_us": med["seq"] * 1e6,
         "sequential_us_p10_p90": [pct(t["seq"], 10), pct(t["seq"], 90)],
         "speedup_vs_sequential": med["seq"] / t_step,
-        "comparators_us": {k: med[k] * 1e6 for k in ("streams", "batched", "ordered", "graph")
-                           if k in med},
+        "comparators_us": {k: med[k] * 1e6 for k in ("streams", "batched", "ordered", "graph",
+                                                      "fused_launch") if k in med},
         "overlap_roofline_us": roof_s * 1e6,
         "overlap_roofline_frac_step": roof_s / t_step,
         "overlap_roofline_frac_kernel": roof_s / t_kern,
@@ -619,9 +629,9 @@ def measure_config(torch, B, inputs, metrics, timer, name, n_dec, steps, warmup,
                  "prefill_items": info["prefill_items"], "decode_items": info["decode_items"],
                  "merge_tasks": info["merge_tasks"],
                  "prefill_quarters_per_cu": info["prefill_quarters_per_cu"],
-                 "sched_mode": info["sched_mode"]},
+                 "sched_mode": info["sched_mode"], "runs_sequential": info["runs_sequential"]},
     }
-    del ordered, graph
+    del ordered, graph, forced
     return runner, batch, spec, counts, t, kern, f
 
 

@@ -169,6 +169,8 @@ typedef struct {
   int32_t one_unit_per_wg;     /* 1: the fused launch runs one workgroup per unit */
   int32_t num_partials;
   int32_t trace_records;
+  int32_t runs_sequential;     /* 1: pod_attn_run runs the prefill and decode
+                                  kernels back to back (see pod_attn_run) */
   uint64_t workspace_bytes;
 } pod_attn_plan_info_t;
 
@@ -337,7 +339,12 @@ pod_status_t pod_attn_plan_scratch(const pod_attn_params_t* params,
  * batch of one kind (no decodes, or no prefill; bf16 or FP8) has nothing to
  * overlap and runs the one kernel it needs with the sequential plan's lists,
  * i.e. what pod_attn_sequential_run runs (unless the plan traces: the trace
- * is indexed by the fused launch's units).  A shared-prefix plan runs its
+ * is indexed by the fused launch's units).  So does, under automatic
+ * scheduling, an MHA batch (Hq == Hkv) too large for the one-unit launch
+ * whose prefill is under a fifth of the planner's work estimate: its prefill items each stream their own KV head
+ * and contend with the decode for HBM, and the fused launch measured slower
+ * there (pod_attn_plan_info_t.runs_sequential reports the choice; any
+ * explicit sched_mode keeps the fused launch).  A shared-prefix plan runs its
  * packed decode kernel.  Asynchronous on `stream`.
  * Errors: POD_ERR_INVALID_ARGUMENT (NULL plan/tensors, a required pointer
  * NULL or not 16-byte aligned, plan without workspace), POD_ERR_HIP. */

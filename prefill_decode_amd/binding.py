@@ -69,7 +69,7 @@ class PlanInfo(C.Structure):
         "seq_prefill_items", "seq_decode_items", "seq_merge_tasks",
         "prefill_splits_max", "decode_splits_max", "wgs_per_cu",
         "prefill_quarters_per_cu", "sched_mode", "one_unit_per_wg", "num_partials",
-        "trace_records")] + \
+        "trace_records", "runs_sequential")] + \
         [("workspace_bytes", C.c_uint64)]
 
 

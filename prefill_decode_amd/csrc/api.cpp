@@ -145,6 +145,13 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
     build_lists(pl->batch, dev, slots, kSeqPrefillHalfItemsPerSlot, 0, 1, t.prefill_kv_splits, 0,
                 &pl->bp, /*decodes_as_prefill=*/true);
   pl->trace_records = (t.flags & POD_FLAG_TRACE) ? pl->fused.n_p() + pl->fused.n_d() : 0;
+  // MHA with a small prefill share: the two kernels back to back
+  // (kMhaSequentialShare); only when the caller left the mode to the planner,
+  // and not for the small batches that run one workgroup per unit (launch
+  // bound: the tiny batch measured 0.99-1.04x fused against sequential)
+  c.runs_sequential = t.sched_mode == POD_SCHED_AUTO && !c.one_unit && np > 0 && nd > 0 &&
+                      params->num_qo_heads == params->num_kv_heads &&
+                      prefill_share_estimate(pl->batch) < kMhaSequentialShare;
   layout_workspace(pl);
   return POD_OK;
 }
@@ -603,7 +610,8 @@ pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t
   // it runs the one kernel it needs with the sequential plan's lists, as the
   // fused launch would only hold units of that kind.  (Traced plans keep the
   // fused launch: the trace is indexed by its units.)
-  if (!pl->has_prefix && !pl->trace_records && (pl->fused.n_p() == 0 || pl->fused.n_d() == 0))
+  if (!pl->has_prefix && !pl->trace_records &&
+      (pl->fused.n_p() == 0 || pl->fused.n_d() == 0 || pl->choice.runs_sequential))
     return run_sequential(pl, t, stream, before_fused, after_fused);
   const WorkLists& w = pl->fused;
   KernelArgs a = make_args(pl, t, w, pl->dl_fused);
@@ -738,6 +746,7 @@ pod_status_t pod_attn_plan_info(pod_attn_plan_t pl, pod_attn_plan_info_t* out) {
   out->one_unit_per_wg = pl->choice.one_unit ? 1 : 0;
   out->num_partials = pl->n_partials;
   out->trace_records = pl->trace_records;
+  out->runs_sequential = pl->choice.runs_sequential ? 1 : 0;
   out->workspace_bytes = pl->ws_bytes;
   return POD_OK;
 }

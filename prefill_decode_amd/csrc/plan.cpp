@@ -107,11 +107,10 @@ pod_status_t validate(const pod_attn_params_t* p, int32_t np, const int32_t* qo,
   return POD_OK;
 }
 
-int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu, int32_t sched_mode) {
+namespace {
+// Estimated prefill and decode times (s) at the expected fractions of the peaks.
+void estimate_times(const Batch& b, double* tp, double* td) {
   const auto& p = b.params;
-  const int32_t full = 4 * wgs_per_cu;
-  if (b.qo.empty()) return 0;
-  if (b.dkv.empty()) return full;
   double pairs_p = 0.0, keys_d = 0.0;
   for (size_t i = 0; i < b.qo.size(); ++i) {
     double q = b.qo[i], k = b.pkv[i];
@@ -121,8 +120,23 @@ int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu, int32_t sched_
   const double f = 4.0 * kHeadDim * p.num_qo_heads * pairs_p;
   const double elem = p.kv_dtype == POD_KV_FP8_E4M3 ? 1.0 : 2.0;   // bytes per K or V element
   const double by = keys_d * p.num_kv_heads * kHeadDim * 2.0 * elem;
-  const double tp = f / (kPeakFlops * kPrefillEff);
-  const double td = by / (kPeakBytes * kDecodeEff);
+  *tp = f / (kPeakFlops * kPrefillEff);
+  *td = by / (kPeakBytes * kDecodeEff);
+}
+}  // namespace
+
+double prefill_share_estimate(const Batch& b) {
+  double tp = 0.0, td = 0.0;
+  estimate_times(b, &tp, &td);
+  return tp + td > 0.0 ? tp / (tp + td) : 0.0;
+}
+
+int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu, int32_t sched_mode) {
+  const int32_t full = 4 * wgs_per_cu;
+  if (b.qo.empty()) return 0;
+  if (b.dkv.empty()) return full;
+  double tp = 0.0, td = 0.0;
+  estimate_times(b, &tp, &td);
   // rounded down: a prefill CU too many starves the decode, whose rate per CU
   // is capped, while one too few only delays the prefill until the decode
   // CUs join it (FP8 70B layer: 5 against 6 eighths, 1,431 against 1,667 us;

@@ -128,7 +128,21 @@ struct PlanChoice {
   int32_t prefill_quarters = 4;        // target prefill WGs per CU, in quarters
   int32_t sched_mode = POD_SCHED_SPLIT;   // resolved mode (never AUTO)
   bool one_unit = false;               // fused launch of one workgroup per unit
+  bool runs_sequential = false;        // pod_attn_run runs the two kernels back to back
 };
+
+// MHA batches (one query head per KV head) whose prefill is under this share
+// of the estimated work run the prefill and decode kernels back to back in
+// pod_attn_run (automatic scheduling, persistent launches only).  Each prefill item of an MHA batch
+// reads its own KV head, so at long contexts its prefill streams nearly as
+// many bytes per FLOP as the decode: the two halves contend for HBM and the
+// fused launch has no idle unit to fill.  Measured on 32/32-head layers with
+// 128 decodes of 8,192 keys and one chunk at 12,288 keys, fused against
+// sequential: bf16 0.98 / 0.97 / 0.91 / 0.95 / 1.04 at prefill shares 0.02 /
+// 0.04 / 0.08 / 0.15 / 0.24, FP8 0.88 / 0.95 / 0.98 / 0.98 / 1.10 at 0.04 /
+// 0.08 / 0.15 / 0.25 / 0.38, and no prefill share or role mode (1-3 eighths,
+// co-located) made the fused launch faster below 0.2.
+constexpr double kMhaSequentialShare = 0.2;
 
 // Automatic launch shape: batches of at most kOneUnitSlotsFactor fused units
 // (prefill items + decode groups) per workgroup slot run one workgroup per
@@ -148,6 +162,8 @@ pod_status_t validate(const pod_attn_params_t* p, int32_t np, const int32_t* qo,
 // workgroup slots (COLOCATE) or eighths of the CUs (SPLIT) given to prefill,
 // from estimated prefill and decode times.
 int32_t auto_prefill_quarters(const Batch& b, int32_t wgs_per_cu, int32_t sched_mode);
+// The prefill's share tp / (tp + td) of the estimated prefill and decode times.
+double prefill_share_estimate(const Batch& b);
 
 // Builds one set of work lists.  `prefill_slots` / `decode_wave_slots` are the
 // concurrent prefill workgroups / decode wavefronts the splits should fill

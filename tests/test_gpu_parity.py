@@ -284,3 +284,24 @@ def test_single_kind_batch(which):
     info = rt.plan.info()
     assert len(tr) == info["trace_records"] == info["prefill_items"] + info["decode_items"] > 0
     assert np.all(tr[:, 5] >= tr[:, 4]) and np.all(tr[:, 4] > 0)     # t_end >= t_start > 0
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_mha_small_prefill_runs_sequentially(kv_dtype):
+    """An MHA batch with a small prefill share: pod_attn_run runs the two
+    kernels back to back (bitwise the sequential result); an explicit
+    scheduler mode keeps the fused launch; both match the oracle."""
+    spec = S(f"mha_routed_{kv_dtype}", 32, 32, [(64, 2048)], [1024] * 128, seed=231,
+             kv_dtype=kv_dtype)
+    say(f"[routed] {spec.name}")
+    b = inputs.make_batch_host(spec, poison=True)
+    ref = oracle.batch_attention(b)
+    r = B.BatchRunner(b)
+    assert r.plan.info()["runs_sequential"] == 1
+    f, s_ = run_path(r, "fused"), run_path(r, "seq")
+    compare(f, ref, f"{spec.name}/fused (routed)")
+    for k in f:
+        assert np.array_equal(f[k], s_[k]), k
+    rf = B.BatchRunner(b, B.make_tuning(sched_mode=B.SCHED_SPLIT))
+    assert rf.plan.info()["runs_sequential"] == 0
+    compare(run_path(rf, "fused"), ref, f"{spec.name}/fused launch")

@@ -367,3 +367,21 @@ def test_ordered_mode_takes_the_sequential_lists():
         ps = _spec_lists(spec)
         for a, b in ((0, 3), (1, 4), (2, 5)):
             assert np.array_equal(po.export(a), ps.export(b)), (name, a)
+
+
+def test_mha_small_prefill_share_runs_sequentially():
+    # automatic scheduling routes an MHA batch with a small prefill share and
+    # too many units for the one-unit launch to the two kernels back to back
+    def routed(spec, **tun):
+        p = B.make_params(spec.num_qo_heads, spec.num_kv_heads, spec.layout, spec.page_size,
+                          spec.causal, spec.sm_scale, kv_dtype=spec.kv_dtype)
+        t = B.make_tuning(**tun) if tun else None
+        return B.plan_host(p, spec.prefill_qo_len, spec.prefill_kv_len, spec.decode_kv_len,
+                           t).info()["runs_sequential"]
+    assert routed(inputs.config_spec("llama2_7b")) == 1
+    assert routed(inputs.config_spec("llama2_7b_fp8")) == 1
+    assert routed(inputs.config_spec("llama2_7b"), sched_mode=B.SCHED_SPLIT) == 0
+    for name in ("tiny", "llama3_8b", "l70b_tp1", "batched"):       # GQA, or one-unit
+        assert routed(inputs.config_spec(name)) == 0, name
+    big = inputs.custom_spec("mha_big_prefill", 32, 32, [(4096, 12288)], [8192] * 128, seed=1)
+    assert routed(big) == 0                                          # share ~0.24
