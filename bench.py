@@ -132,6 +132,36 @@ def _cpu_model():
     return "unknown"
 
 
+def _blas_build():
+    """numpy's BLAS library and version, as numpy reports its build."""
+    try:
+        b = np.__config__.CONFIG["Build Dependencies"]["blas"]
+        return f"{b.get('name', '?')} {b.get('version', '?')}"
+    except (AttributeError, KeyError, TypeError):
+        return "unknown"
+
+
+def device_info(torch):
+    """The GPU and its clocks at the start of the run: the device properties
+    torch reports and the current shader / memory clock levels from
+    `rocm-smi --showclocks --json` (None when the tool is not there or fails;
+    it only reads)."""
+    import subprocess
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1), "clocks": None}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        card = next(iter(json.loads(r.stdout).values()))
+        info["clocks"] = {k: v for k, v in card.items()
+                          if k.lower().startswith(("sclk", "mclk", "fclk"))}
+    except (OSError, subprocess.SubprocessError, ValueError, StopIteration, AttributeError):
+        pass
+    return info
+
+
 def _row_pairs(spec):
     """Visible keys of every prefill row (global order) and of every decode."""
     rows = []
@@ -180,7 +210,10 @@ def cpu_baseline(batch_dev, spec, budget_s=15.0):
     frac = min(1.0, budget_s * rate / total)
     dt, pairs, nr, nd = timed(frac)
     est = dt * total / max(pairs, 1.0)
+    from prefill_decode_amd import metrics
+    flops = metrics.algorithmic_counts(spec)["flops"]
     return {"value": est * 1e6, "unit": "µs/layer", "cores": workers, "kind": "oracle",
+            "gflops_fp64": flops / est / 1e9, "blas": _blas_build(),
             "sample": f"{nr} of {n_rows} prefill rows and {nd} of {n_dec} decodes, evenly "
                       f"spaced ({pairs / total:.3g} of the visible query-key pairs), fp64 numpy, "
                       f"{dt:.1f} s, scaled by pairs; BLAS 1 thread per worker; CPU {_cpu_model()}"}
@@ -681,6 +714,7 @@ def main():
     from prefill_decode_amd import inputs, metrics
 
     torch.cuda.set_device(0)
+    device = device_info(torch)
     timer = Timer(torch, not args.no_flush)
     tuning_kw = dict(prefill_quarters_per_cu=args.quarters, sched_mode=args.sched,
                      prefill_kv_splits=args.prefill_splits, decode_kv_splits=args.decode_splits)
@@ -745,6 +779,7 @@ def main():
         "plan": head["plan"],
         "wall_s_timed_loop": wall,
         "roofline": roof,
+        "device": device,
     }
     del runner
     torch.cuda.empty_cache()
