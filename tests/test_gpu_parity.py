@@ -305,3 +305,21 @@ def test_mha_small_prefill_runs_sequentially(kv_dtype):
     rf = B.BatchRunner(b, B.make_tuning(sched_mode=B.SCHED_SPLIT))
     assert rf.plan.info()["runs_sequential"] == 0
     compare(run_path(rf, "fused"), ref, f"{spec.name}/fused launch")
+
+
+def test_empty_batch_every_entry_point():
+    """A batch with no request plans and runs on every path as a no-op: no
+    launch, status OK, and an unrelated canary on the stream is untouched."""
+    import torch
+    spec = S("empty", 8, 2, [], [], seed=301)
+    say("[empty] plan and run an empty batch on every path")
+    b = inputs.make_batch_host(spec)
+    r = B.BatchRunner(b, B.make_tuning(flags=B.FLAG_BATCHED_PREFILL))
+    info = r.plan.info()
+    assert info["prefill_items"] == info["decode_items"] == info["merge_tasks"] == 0
+    canary = torch.full((1024,), 7.0, device="cuda")
+    for path in ("fused", "seq", "streams", "batched"):
+        got = run_path(r, path)
+        assert all(v.size == 0 for v in got.values()), path
+    torch.cuda.synchronize()
+    assert bool((canary == 7.0).all())
