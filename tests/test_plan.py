@@ -385,3 +385,47 @@ def test_mha_small_prefill_share_runs_sequentially():
         assert routed(inputs.config_spec(name)) == 0, name
     big = inputs.custom_spec("mha_big_prefill", 32, 32, [(4096, 12288)], [8192] * 128, seed=1)
     assert routed(big) == 0                                          # share ~0.24
+
+
+def _random_spec(rng, i):
+    """A random small batch: head layout, page size, causal flag, prefill
+    chunks (qo <= kv) and decode lengths drawn from a seeded generator."""
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 16, 24, 32]))
+    np_ = int(rng.integers(0, 5))
+    nd = int(rng.integers(0, 12))
+    if np_ + nd == 0:
+        nd = 1
+    pre = []
+    for _ in range(np_):
+        qo = int(rng.integers(1, 700))
+        pre.append((qo, qo + int(rng.integers(0, 3000))))
+    dec = [int(x) for x in rng.integers(1, 9000, size=nd)]
+    return inputs.custom_spec(f"rand{i}", g * hkv, hkv, pre, dec, seed=9000 + i,
+                              causal=bool(rng.integers(0, 4)),
+                              page_size=int(rng.choice([1, 8, 16, 64])))
+
+
+def test_random_batches_cover_and_partition():
+    """Seeded random batches (head groups 1-32, 0-4 prefill chunks, 0-11
+    decodes, causal or not, page sizes 1-64) under random tunings: every
+    list the planner builds (fused and sequential) covers each (row, head)
+    once, splits partition the visible keys, and every partial slot is
+    merged exactly once."""
+    rng = np.random.default_rng(20261204)
+    for i in range(60):
+        spec = _random_spec(rng, i)
+        tun = {}
+        if rng.integers(0, 2):
+            tun["prefill_kv_splits"] = int(rng.integers(0, 70))
+        if rng.integers(0, 2):
+            tun["decode_kv_splits"] = int(rng.integers(0, 70))
+        if rng.integers(0, 3) == 0:
+            tun["prefill_quarters_per_cu"] = int(rng.integers(0, 9))
+        if rng.integers(0, 3) == 0:
+            tun["sched_mode"] = int(rng.integers(0, 4))
+        pl = _spec_lists(spec, **tun)
+        info = pl.info()
+        for which in ((0, 1, 2, 6), (3, 4, 5, 7)):
+            _check_lists(spec, *(pl.export(w) for w in which), info["num_partials"])
+        pl.destroy()
