@@ -66,7 +66,7 @@ struct pod_attn_plan_s {
 
 namespace {
 
-void layout_workspace(pod_attn_plan_s* pl);
+pod_status_t layout_workspace(pod_attn_plan_s* pl);
 
 pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32_t* qo,
                         const int32_t* pkv, int32_t nd, const int32_t* dkv,
@@ -152,13 +152,17 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   c.runs_sequential = t.sched_mode == POD_SCHED_AUTO && !c.one_unit && np > 0 && nd > 0 &&
                       params->num_qo_heads == params->num_kv_heads &&
                       prefill_share_estimate(pl->batch) < kMhaSequentialShare;
-  layout_workspace(pl);
-  return POD_OK;
+  return layout_workspace(pl);
 }
 
 // Workspace layout of a plan: counters, the work lists, trace, partials.
-void layout_workspace(pod_attn_plan_s* pl) {
+// Refuses lists whose split partials outgrow their int32 indices.
+pod_status_t layout_workspace(pod_attn_plan_s* pl) {
   const WorkLists& sq = pl->seq_is_fused ? pl->fused : pl->seq;
+  if (pl->fused.n_partials < 0 || sq.n_partials < 0 || pl->bp.n_partials < 0)
+    return set_err(POD_ERR_UNSUPPORTED,
+                   "the plan needs more than 2^31 - 1 split partials (force fewer KV splits or "
+                   "plan a smaller batch)");
   pl->n_partials = std::max(std::max(pl->fused.n_partials, sq.n_partials), pl->bp.n_partials);
   size_t off = 0;
   pl->off_counters = off;
@@ -184,6 +188,7 @@ void layout_workspace(pod_attn_plan_s* pl) {
   pl->off_part_o = off;
   off = align_up(off + (size_t)pl->n_partials * kHeadDim * sizeof(float));
   pl->ws_bytes = off;
+  return POD_OK;
 }
 
 pod_status_t query_device(pod_device_desc_t* dev, int* device) {
@@ -375,7 +380,7 @@ pod_status_t build_prefix_plan(const pod_attn_params_t* params, int32_t nd, cons
                        &pl->members);
     pl->has_prefix = true;
     pl->trace_records = 0;
-    layout_workspace(pl);
+    if ((st = layout_workspace(pl)) != POD_OK) return st;
   } catch (const std::exception& ex) {
     return set_err(POD_ERR_INTERNAL, ex.what());
   }

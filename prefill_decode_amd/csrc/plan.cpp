@@ -169,7 +169,7 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
   const int32_t hq = p.num_qo_heads, hkv = p.num_kv_heads, g = hq / hkv;
   const int32_t np = (int32_t)b.qo.size(), nd = (int32_t)b.dkv.size();
   WorkLists w;
-  int32_t n_partials = 0;
+  int64_t n_partials = 0;   // checked against the int32 indices at the end
 
   // ---- prefill items (request, group of nh query heads, block of npos
   // positions); nh * npos = kPrefillRows ----
@@ -231,7 +231,7 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
     int32_t base = -1;
     const bool dec_tile = t.req >= np;
     if (s > 1) {
-      base = n_partials;
+      base = (int32_t)n_partials;
       n_partials += s * kPrefillRows;
       const size_t at = w.m_tasks.size();
       w.m_tasks.resize(at + (size_t)M_FIELDS * nh * t.nrows);
@@ -314,8 +314,8 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
     s = (int32_t)ceil_div(steps, per);
     int32_t region = -1;
     if (s > 1) {
-      region = n_partials;
-      n_partials += hq * s;
+      region = (int32_t)n_partials;
+      n_partials += (int64_t)hq * s;
       for (int32_t h = 0; h < hq; ++h) {
         w.m_tasks.push_back(i * hq + h);
         w.m_tasks.push_back(region + h * s);
@@ -345,7 +345,9 @@ void build_lists(const Batch& b, const pod_device_desc_t& dev, int64_t prefill_s
                    [](const DI& a, const DI& c) { return a.work > c.work; });
   w.d_items.reserve(ditems.size() * D_FIELDS);
   for (auto& it : ditems) w.d_items.insert(w.d_items.end(), it.f.begin(), it.f.end());
-  w.n_partials = n_partials;
+  // partial indices are int32 (work-list fields and kernel arithmetic): a
+  // larger count marks the lists unusable (the caller refuses the plan)
+  w.n_partials = n_partials <= INT32_MAX ? (int32_t)n_partials : -1;
   *out = std::move(w);
 }
 
@@ -407,7 +409,7 @@ void build_prefix_lists(const Batch& b, const std::vector<int32_t>& group_of,
   };
   WorkLists w;
   members->clear();
-  int32_t n_partials = 0;
+  int64_t n_partials = 0;   // checked against the int32 indices at the end
   struct DI { std::array<int32_t, D_FIELDS> f; int32_t work; };
   std::vector<DI> tiles, items;
   for (const G& gr : groups) {
@@ -418,8 +420,8 @@ void build_prefix_lists(const Batch& b, const std::vector<int32_t>& group_of,
     int32_t ss_max = 0;
     for (int32_t r : gr.m) ss_max = std::max(ss_max, splits_of(b.dkv[r] - gr.plen, chunk).first);
     const int32_t smax = sp + ss_max;
-    const int32_t gbase = n_partials;
-    n_partials += (int32_t)gr.m.size() * hq * smax;
+    const int32_t gbase = (int32_t)n_partials;
+    n_partials += (int64_t)gr.m.size() * hq * smax;
     auto region = [&](int32_t rl, int32_t h) { return gbase + (rl * hq + h) * smax; };
     const int32_t nm = (int32_t)gr.m.size();
     for (int32_t kh = 0; kh < hkv; ++kh)
@@ -470,7 +472,9 @@ void build_prefix_lists(const Batch& b, const std::vector<int32_t>& group_of,
   for (auto& it : tiles) w.p_items.insert(w.p_items.end(), it.f.begin(), it.f.end());
   for (auto& it : items) w.d_items.insert(w.d_items.end(), it.f.begin(), it.f.end());
   w.pool_off = {0, w.n_p()};
-  w.n_partials = n_partials;
+  // partial indices are int32 (work-list fields and kernel arithmetic): a
+  // larger count marks the lists unusable (the caller refuses the plan)
+  w.n_partials = n_partials <= INT32_MAX ? (int32_t)n_partials : -1;
   *out = std::move(w);
 }
 

@@ -156,3 +156,16 @@ def test_one_hip_runtime_whatever_the_import_order():
                        cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert r.returncode == 0, r.stderr[-500:]
     assert r.stdout.strip().splitlines()[-1] == "1", r.stdout
+
+
+def test_plan_refuses_partials_beyond_int32():
+    """A batch whose split partials would outgrow their int32 indices (one
+    non-causal chunk of 2^19 rows, 64 query heads, 64 forced KV splits:
+    2^31 partial rows) is refused with POD_ERR_UNSUPPORTED; one row fewer
+    per tile's share (2^19 - 64 rows) plans."""
+    p = B.make_params(64, 8, causal=False)
+    t = B.make_tuning(prefill_kv_splits=64, match_sequential=1)
+    n = 1 << 19
+    st = _plan_status(p, [n], [n], [], t)
+    assert st == UNS and "2^31 - 1 split partials" in B.last_error(), (st, B.last_error())
+    assert _plan_status(p, [n - 64], [n - 64], [], t) == OK, B.last_error()
