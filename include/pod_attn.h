@@ -242,7 +242,9 @@ typedef struct {
  * Errors: POD_ERR_INVALID_ARGUMENT (lengths, heads, scale, layout, dtype,
  * NULL length arrays with a nonzero count), POD_ERR_UNSUPPORTED (head_dim !=
  * 128, wgs_per_cu other than 0 or 2, an FP8 cache with pages of fewer than
- * 16 tokens, or with the batched-prefill comparator),
+ * 16 tokens, or with the batched-prefill comparator, a kv_len above 2^24,
+ * more than 2^31 - 1 (row, head) outputs, or KV splits whose partials
+ * would number more than 2^31 - 1),
  * POD_ERR_WORKSPACE_TOO_SMALL, POD_ERR_HIP.  With an FP8 cache every run
  * entry point runs the FP8 forms of its kernels (fused: the FP8 prefill tile
  * beside the FP8 decode unit). */
