@@ -78,9 +78,10 @@ typedef enum { POD_KV_BF16 = 0, POD_KV_FP8_E4M3 = 1 } pod_kv_dtype_t;
  * own runs dry, so all modes run every unit exactly once). */
 typedef enum {
   /* The planner's choice: for a batch of at most two fused units (prefill
-   * items + decode groups) per workgroup slot, POD_SCHED_COLOCATE with one
-   * workgroup per unit (POD_FLAG_ONE_UNIT_PER_WG); otherwise POD_SCHED_SPLIT
-   * with persistent workgroups. */
+   * items + decode groups) per workgroup slot, one workgroup per unit
+   * (POD_FLAG_ONE_UNIT_PER_WG) with POD_SCHED_COLOCATE roles when the batch
+   * has one prefill request and POD_SCHED_SPLIT roles when it has several;
+   * otherwise POD_SCHED_SPLIT with persistent workgroups. */
   POD_SCHED_AUTO = 0,
   /* Co-location on every CU: the CU's workgroups take roles in arrival
    * order (a per-CU ticket), the first prefill_quarters_per_cu / 4 of them

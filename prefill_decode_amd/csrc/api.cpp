@@ -116,10 +116,15 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
                 kFusedDecodeUnitsPerWave, t.prefill_kv_splits, t.decode_kv_splits, &pl->fused);
   }
   // automatic launch shape (kOneUnitSlotsFactor): a small batch runs one
-  // workgroup per unit with per-CU tickets; its lists are rebuilt for the
-  // co-location share
-  if (t.sched_mode == POD_SCHED_AUTO && !c.one_unit &&
+  // workgroup per unit.  With several prefill requests each workgroup takes
+  // its role from its CU index, as the persistent CU partition does, over
+  // the same lists; with one, from its CU's ticket, over lists rebuilt for
+  // the co-location share (measurements at kOneUnitSlotsFactor)
+  if (t.sched_mode == POD_SCHED_AUTO && !c.one_unit && np > 1 &&
       (int64_t)pl->fused.n_p() + pl->fused.n_groups() <= kOneUnitSlotsFactor * slots) {
+    c.one_unit = true;
+  } else if (t.sched_mode == POD_SCHED_AUTO && !c.one_unit &&
+             (int64_t)pl->fused.n_p() + pl->fused.n_groups() <= kOneUnitSlotsFactor * slots) {
     c.sched_mode = POD_SCHED_COLOCATE;
     c.one_unit = true;
     if (t.prefill_quarters_per_cu < 0)

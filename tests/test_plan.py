@@ -227,13 +227,17 @@ def test_proportional_mix():
     info = {n: _spec_lists(inputs.config_spec(n)).info() for n in inputs.CONFIG_NAMES}
     q = {n: i["prefill_quarters_per_cu"] for n, i in info.items()}
     for n, i in info.items():
-        # automatic launch shape: one workgroup per unit (co-located roles)
-        # for at most two fused units per workgroup slot, else persistent
-        # CU partition
+        # automatic launch shape: one workgroup per unit for at most two
+        # fused units per workgroup slot (co-located roles with one prefill
+        # request, CU-partition roles with several), else persistent CU
+        # partition
         small = i["prefill_items"] + i["decode_groups"] <= 2 * 512
         assert i["one_unit_per_wg"] == int(small), n
-        if small:
+        several = len(inputs.config_spec(n).prefill_qo_len) > 1
+        if small and not several:
             assert i["sched_mode"] == B.SCHED_COLOCATE and 1 <= q[n] <= 7, n
+        elif small:
+            assert i["sched_mode"] == B.SCHED_SPLIT and 3 <= q[n] <= 6, n
         else:
             # CU partition: 3..6 eighths of the CUs start on prefill
             assert i["sched_mode"] == B.SCHED_SPLIT and 3 <= q[n] <= 6, n
@@ -429,3 +433,18 @@ def test_random_batches_cover_and_partition():
         for which in ((0, 1, 2, 6), (3, 4, 5, 7)):
             _check_lists(spec, *(pl.export(w) for w in which), info["num_partials"])
         pl.destroy()
+
+
+def test_one_unit_roles_follow_prefill_request_count():
+    """Small batches run one workgroup per unit: with co-located roles for one
+    prefill request, with the CU partition's roles (and its lists) for
+    several; an explicit mode keeps the persistent launch."""
+    for nd in (32, 64, 96):
+        spec = inputs.config_spec("batched", n_dec=nd)
+        i = _spec_lists(spec).info()
+        f = _spec_lists(spec, sched_mode=B.SCHED_SPLIT)
+        assert i["one_unit_per_wg"] == 1 and i["sched_mode"] == B.SCHED_SPLIT, nd
+        assert np.array_equal(_spec_lists(spec).export(0), f.export(0))
+        assert f.info()["one_unit_per_wg"] == 0
+    i = _spec_lists(inputs.config_spec("llama3_8b")).info()
+    assert i["one_unit_per_wg"] == 1 and i["sched_mode"] == B.SCHED_COLOCATE
