@@ -233,7 +233,8 @@ def pmc_run(args):
     batch = inputs.make_batch_device(spec)
     runner = B.BatchRunner(batch)
     if runner.plan.info()["runs_sequential"]:
-        # the plan runs the two kernels back to back: count the fused launch itself
+        # the plan runs the two kernels back to back or on two streams: count
+        # the fused launch itself
         runner = B.BatchRunner(batch, B.make_tuning(sched_mode=B.SCHED_SPLIT))
     for _ in range(args.steps):
         runner.run()
@@ -495,8 +496,9 @@ PATH_NAMES = {
                "queue, prefill units first",
     "graph": "pod_attn_run captured once into a HIP graph and replayed (the fused kernel's "
              "self-resetting counters; no launch overhead per kernel)",
-    "fused_launch": "where the plan runs the two kernels back to back (plan.runs_sequential), "
-                    "the fused launch itself (an explicit scheduler mode)",
+    "fused_launch": "where the plan runs the two kernels back to back or on two streams "
+                    "(plan.runs_sequential 1 or 2), the fused launch itself (an explicit "
+                    "scheduler mode)",
 }
 
 

@@ -171,7 +171,9 @@ typedef struct {
   int32_t num_partials;
   int32_t trace_records;
   int32_t runs_sequential;     /* 1: pod_attn_run runs the prefill and decode
-                                  kernels back to back (see pod_attn_run) */
+                                  kernels back to back; 2: at once, on the
+                                  caller's stream and the library's second
+                                  stream on the device (see pod_attn_run) */
   uint64_t workspace_bytes;
 } pod_attn_plan_info_t;
 
@@ -346,8 +348,16 @@ pod_status_t pod_attn_plan_scratch(const pod_attn_params_t* params,
  * scheduling, an MHA batch (Hq == Hkv) too large for the one-unit launch
  * whose prefill is under a fifth of the planner's work estimate: its prefill items each stream their own KV head
  * and contend with the decode for HBM, and the fused launch measured slower
- * there (pod_attn_plan_info_t.runs_sequential reports the choice; any
- * explicit sched_mode keeps the fused launch).  A shared-prefix plan runs its
+ * there.  A GQA batch (Hq > Hkv) with several prefill requests, too large
+ * for the one-unit launch, whose prefill is under 0.15 of the estimate runs
+ * the two kernels at once, the prefill kernel on `stream` and the decode
+ * kernel on a second stream, forked from and joined back to `stream` by
+ * events, as pod_attn_streams_run does (the library creates that stream, at
+ * default priority, when the first such plan is made on a device, and keeps
+ * it until the process ends; plans on the device share it): each kernel keeps its own
+ * register and LDS footprint, which measured faster than the fused launch on
+ * such decode-heavy batches (pod_attn_plan_info_t.runs_sequential reports the
+ * choice; any explicit sched_mode keeps the fused launch).  A shared-prefix plan runs its
  * packed decode kernel.  Asynchronous on `stream`.
  * Errors: POD_ERR_INVALID_ARGUMENT (NULL plan/tensors, a required pointer
  * NULL or not 16-byte aligned, plan without workspace), POD_ERR_HIP. */

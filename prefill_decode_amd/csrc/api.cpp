@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -54,6 +55,7 @@ struct pod_attn_plan_s {
   DevLists dl_fused, dl_seq, dl_bp;
   // two-stream comparator: fork / join events (created on first use)
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipStream_t aux = nullptr;   // two-stream plans: the device's second stream (not owned)
   uint64_t launches[2] = {0, 0};   // successful launches per kind (counter parity)
   size_t ws_bytes = 0;
   char* ws = nullptr;          // caller-owned device buffer (NULL: host-only plan)
@@ -67,6 +69,27 @@ struct pod_attn_plan_s {
 namespace {
 
 pod_status_t layout_workspace(pod_attn_plan_s* pl);
+
+// The second stream pod_attn_run uses for plans that run the prefill and
+// decode kernels at once: one per device, created (default priority,
+// non-blocking) by the first such plan on that device, with the device
+// current, and kept until the process ends.  Plans share it: their decode
+// kernels queue on it in the order their runs enqueue them.
+hipError_t aux_stream(int device, hipStream_t* out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static hipStream_t streams[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[device]) {
+    hipStream_t s = nullptr;
+    const hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+    streams[device] = s;
+  }
+  *out = streams[device];
+  return hipSuccess;
+}
 
 pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32_t* qo,
                         const int32_t* pkv, int32_t nd, const int32_t* dkv,
@@ -154,9 +177,15 @@ pod_status_t build_plan(const pod_attn_params_t* params, int32_t np, const int32
   // (kMhaSequentialShare); only when the caller left the mode to the planner,
   // and not for the small batches that run one workgroup per unit (launch
   // bound: the tiny batch measured 0.99-1.04x fused against sequential)
-  c.runs_sequential = t.sched_mode == POD_SCHED_AUTO && !c.one_unit && np > 0 && nd > 0 &&
-                      params->num_qo_heads == params->num_kv_heads &&
-                      prefill_share_estimate(pl->batch) < kMhaSequentialShare;
+  // GQA with several prefill requests and a small prefill share: the two
+  // kernels at once on two streams (kGqaStreamsShare)
+  if (t.sched_mode == POD_SCHED_AUTO && !c.one_unit && np > 0 && nd > 0) {
+    const double share = prefill_share_estimate(pl->batch);
+    if (params->num_qo_heads == params->num_kv_heads && share < kMhaSequentialShare)
+      c.runs_sequential = 1;
+    else if (params->num_qo_heads > params->num_kv_heads && np > 1 && share < kGqaStreamsShare)
+      c.runs_sequential = 2;
+  }
   return layout_workspace(pl);
 }
 
@@ -418,6 +447,13 @@ pod_status_t finish_device_plan(pod_attn_plan_s* pl, int device, void* workspace
   }
   pl->ws = (char*)workspace;
   pl->device = device;
+  if (pl->choice.runs_sequential == 2) {
+    const hipError_t es = aux_stream(device, &pl->aux);
+    if (es != hipSuccess) {
+      delete pl;
+      return hip_err(es, "hipStreamCreateWithFlags (second stream)");
+    }
+  }
   hipError_t e = hipMemsetAsync(pl->ws + pl->off_counters, 0, kCounterInts * sizeof(int32_t), stream);
   if (e != hipSuccess) {
     delete pl;
@@ -611,6 +647,56 @@ pod_status_t run_sequential(pod_attn_plan_t pl, const pod_attn_tensors_t* t, hip
 
 }  // namespace
 
+namespace {
+
+// Prefill kernel on `stream`, decode kernel on `decode_stream` (forked from
+// and joined back to `stream` by events), then the merge on `stream`;
+// `before` / `after` (may be NULL) are recorded on `stream` around the two
+// kernels.
+pod_status_t run_streams(pod_attn_plan_t pl, const pod_attn_tensors_t* t, hipStream_t stream,
+                         hipStream_t decode_stream, hipEvent_t before, hipEvent_t after) {
+  const WorkLists& w = pl->seq_is_fused ? pl->fused : pl->seq;
+  KernelArgs a = make_args(pl, t, w, pl->dl_seq);
+  pick_counters(pl, kKindSeq, stream, &a);
+  // the decode kernel claims from a counter block of its own (the fused
+  // kind's, which a plan run this way does not launch): the two kernels run
+  // at once, and a captured (self-resetting) launch resets its whole block
+  // when its last workgroup ends
+  KernelArgs ad = a;
+  pick_counters(pl, kKindFused, stream, &ad);
+  hipError_t e;
+  for (hipEvent_t* ev : {&pl->ev_fork, &pl->ev_join})
+    if (!*ev && (e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess)
+      return hip_err(e, "hipEventCreateWithFlags");
+  if (before && (e = hipEventRecord(before, stream)) != hipSuccess)
+    return hip_err(e, "hipEventRecord(before)");
+  // the decode stream starts after the work already enqueued on `stream`
+  if ((e = hipEventRecord(pl->ev_fork, stream)) != hipSuccess) return hip_err(e, "hipEventRecord");
+  if ((e = hipStreamWaitEvent(decode_stream, pl->ev_fork, 0)) != hipSuccess)
+    return hip_err(e, "hipStreamWaitEvent");
+  const int kvm = kv_mode_of(pl);
+  if (w.n_p() > 0) {
+    if ((e = launch_prefill(a, kvm, w.n_p(), stream)) != hipSuccess)
+      return hip_err(e, "prefill kernel launch");
+    if (!a.self_reset) ++pl->launches[kKindSeq];
+  }
+  if (w.n_groups() > 0 &&
+      (e = is_fp8(pl) ? launch_decode_fp8(ad, kvm, w.n_groups(), decode_stream)
+                      : launch_decode(ad, kvm, w.n_groups(), decode_stream)) != hipSuccess)
+    return hip_err(e, "decode kernel launch");
+  if (w.n_groups() > 0 && !ad.self_reset) ++pl->launches[kKindFused];
+  // join: the merge (and whatever the caller enqueues next) waits for both
+  if ((e = hipEventRecord(pl->ev_join, decode_stream)) != hipSuccess)
+    return hip_err(e, "hipEventRecord");
+  if ((e = hipStreamWaitEvent(stream, pl->ev_join, 0)) != hipSuccess)
+    return hip_err(e, "hipStreamWaitEvent");
+  if (after && (e = hipEventRecord(after, stream)) != hipSuccess)
+    return hip_err(e, "hipEventRecord(after)");
+  return launch_merge_of(a, w, stream);
+}
+
+}  // namespace
+
 pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t,
                                  hipStream_t stream, hipEvent_t before_fused,
                                  hipEvent_t after_fused) {
@@ -620,6 +706,9 @@ pod_status_t pod_attn_run_events(pod_attn_plan_t pl, const pod_attn_tensors_t* t
   // it runs the one kernel it needs with the sequential plan's lists, as the
   // fused launch would only hold units of that kind.  (Traced plans keep the
   // fused launch: the trace is indexed by its units.)
+  if (!pl->has_prefix && !pl->trace_records && pl->choice.runs_sequential == 2 && pl->aux &&
+      pl->fused.n_p() > 0 && pl->fused.n_d() > 0 && stream != pl->aux)
+    return run_streams(pl, t, stream, pl->aux, before_fused, after_fused);
   if (!pl->has_prefix && !pl->trace_records &&
       (pl->fused.n_p() == 0 || pl->fused.n_d() == 0 || pl->choice.runs_sequential))
     return run_sequential(pl, t, stream, before_fused, after_fused);
@@ -667,33 +756,7 @@ pod_status_t pod_attn_streams_run(pod_attn_plan_t pl, const pod_attn_tensors_t* 
   if (st != POD_OK) return st;
   if (decode_stream == stream)
     return set_err(POD_ERR_INVALID_ARGUMENT, "decode_stream must differ from stream");
-  const WorkLists& w = pl->seq_is_fused ? pl->fused : pl->seq;
-  KernelArgs a = make_args(pl, t, w, pl->dl_seq);
-  pick_counters(pl, kKindSeq, stream, &a);
-  hipError_t e;
-  for (hipEvent_t* ev : {&pl->ev_fork, &pl->ev_join})
-    if (!*ev && (e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess)
-      return hip_err(e, "hipEventCreateWithFlags");
-  // the decode stream starts after the work already enqueued on `stream`
-  if ((e = hipEventRecord(pl->ev_fork, stream)) != hipSuccess) return hip_err(e, "hipEventRecord");
-  if ((e = hipStreamWaitEvent(decode_stream, pl->ev_fork, 0)) != hipSuccess)
-    return hip_err(e, "hipStreamWaitEvent");
-  const int kvm = kv_mode_of(pl);
-  if (w.n_p() > 0) {
-    if ((e = launch_prefill(a, kvm, w.n_p(), stream)) != hipSuccess)
-      return hip_err(e, "prefill kernel launch");
-    if (!a.self_reset) ++pl->launches[kKindSeq];
-  }
-  if (w.n_groups() > 0 &&
-      (e = is_fp8(pl) ? launch_decode_fp8(a, kvm, w.n_groups(), decode_stream)
-                      : launch_decode(a, kvm, w.n_groups(), decode_stream)) != hipSuccess)
-    return hip_err(e, "decode kernel launch");
-  // join: the merge (and whatever the caller enqueues next) waits for both
-  if ((e = hipEventRecord(pl->ev_join, decode_stream)) != hipSuccess)
-    return hip_err(e, "hipEventRecord");
-  if ((e = hipStreamWaitEvent(stream, pl->ev_join, 0)) != hipSuccess)
-    return hip_err(e, "hipStreamWaitEvent");
-  return launch_merge_of(a, w, stream);
+  return run_streams(pl, t, stream, decode_stream, nullptr, nullptr);
 }
 
 pod_status_t pod_attn_batched_prefill_run(pod_attn_plan_t pl, const pod_attn_tensors_t* t,
@@ -756,7 +819,7 @@ pod_status_t pod_attn_plan_info(pod_attn_plan_t pl, pod_attn_plan_info_t* out) {
   out->one_unit_per_wg = pl->choice.one_unit ? 1 : 0;
   out->num_partials = pl->n_partials;
   out->trace_records = pl->trace_records;
-  out->runs_sequential = pl->choice.runs_sequential ? 1 : 0;
+  out->runs_sequential = pl->choice.runs_sequential;
   out->workspace_bytes = pl->ws_bytes;
   return POD_OK;
 }

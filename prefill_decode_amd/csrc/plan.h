@@ -128,7 +128,8 @@ struct PlanChoice {
   int32_t prefill_quarters = 4;        // target prefill WGs per CU, in quarters
   int32_t sched_mode = POD_SCHED_SPLIT;   // resolved mode (never AUTO)
   bool one_unit = false;               // fused launch of one workgroup per unit
-  bool runs_sequential = false;        // pod_attn_run runs the two kernels back to back
+  int32_t runs_sequential = 0;         // pod_attn_run runs the two kernels back to back (1)
+                                       // or at once on two streams (2)
 };
 
 // MHA batches (one query head per KV head) whose prefill is under this share
@@ -143,6 +144,25 @@ struct PlanChoice {
 // 0.08 / 0.15 / 0.25 / 0.38, and no prefill share or role mode (1-3 eighths,
 // co-located) made the fused launch faster below 0.2.
 constexpr double kMhaSequentialShare = 0.2;
+
+// GQA batches with several prefill requests whose prefill is under this
+// share of the estimated work run the prefill and decode kernels at once on
+// two streams in pod_attn_run (automatic scheduling, persistent launches
+// only).  Each kernel keeps its own register and LDS footprint (the decode
+// workgroups are not held to the fused kernel's prefill-sized allocation),
+// and the hardware fills the CUs from both grids.  Measured, fused / two
+// streams / sequential (us, interleaved): the batched mix's prefill with 256
+// decodes (estimated share 0.11) 1,595 / 1,527 / 1,608; with 192 (0.09)
+// 1,181 / 1,188 / 1,232 on one box and 1,227-1,253 / 1,200 / 1,246-1,254 in
+// two bench runs; eight 128-token chunks + 200 decodes (0.08) 1,279 / 1,247 /
+// 1,226; two 512-token chunks + 160 decodes (0.12) 1,039 / 1,031 / 1,016;
+// one 512-token chunk + 256 decodes (0.06) 1,459 / 1,421 / 1,423 (one
+// request: not routed).  Between 0.15 and 0.2 the two shapes did not agree:
+// two streams led with 128 decodes (0.17: 838 / 795 / 835) and on the FP8
+// mix (0.16: 715 / 696 / 771), the fused launch on a 64-head layer with two
+// 256-token chunks and 256 decodes (0.16: 1,307 / 1,334 / 1,332); the bound
+// sits below all three.
+constexpr double kGqaStreamsShare = 0.15;
 
 // Automatic launch shape: batches of at most kOneUnitSlotsFactor fused units
 // (prefill items + decode groups) per workgroup slot run one workgroup per

@@ -112,3 +112,54 @@ def test_batched_prefill_needs_its_flag():
     with pytest.raises(B.PodError) as e:
         runner.batched_prefill_run()
     assert e.value.status == 1
+
+
+def test_gqa_small_prefill_runs_on_two_streams():
+    """The batched mix at full size (four prefill requests, a prefill share
+    of 0.09): pod_attn_run runs the prefill and decode kernels at once on two
+    streams.  Its outputs equal pod_attn_streams_run's and the sequential
+    run's bitwise (same kernels, same lists), match the fp64 oracle on
+    sampled rows, and a graph capture of it (the fork onto the library's
+    second stream and the join inside the capture) replays to the same bits,
+    with eager runs between the replays."""
+    import torch
+    spec = inputs.config_spec("batched")
+    say("[two-stream route] batched: generating on device")
+    bd = inputs.make_batch_device(spec, poison=True)
+    r = B.BatchRunner(bd)
+    assert r.plan.info()["runs_sequential"] == 2
+    fused = run_path(r, "fused")
+    for path in ("streams", "seq"):
+        other = run_path(r, path)
+        for k in fused:
+            assert np.array_equal(fused[k], other[k]), (path, k)
+    rows = [0, 127, 128, 383, 384, 895, 896, 1535]
+    dec = [0, 1, 95, 191]
+    sub = inputs.host_subset(bd, list(range(spec.num_prefill)), dec)
+    ref = oracle.sample_batch_attention(sub, rows, list(range(len(dec))))
+    compare({"o_prefill": fused["o_prefill"][rows], "lse_prefill": fused["lse_prefill"][rows],
+             "o_decode": fused["o_decode"][dec], "lse_decode": fused["lse_decode"][dec]},
+            ref, "batched/two-stream route")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        r.run()
+    torch.cuda.synchronize()
+    for i in range(3):
+        say(f"  graph replay {i}")
+        for t in (r.o_prefill, r.o_decode, r.lse_prefill, r.lse_decode):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = r.outputs()
+        for k in fused:
+            assert np.array_equal(got[k], fused[k]), ("replay", i, k)
+        eager = run_path(r, "fused")
+        for k in fused:
+            assert np.array_equal(eager[k], fused[k]), ("eager after replay", i, k)
+    f = B.BatchRunner(bd, B.make_tuning(sched_mode=B.SCHED_SPLIT))
+    assert f.plan.info()["runs_sequential"] == 0
+    del r, f, bd
+    torch.cuda.empty_cache()

@@ -385,7 +385,7 @@ def test_mha_small_prefill_share_runs_sequentially():
     assert routed(inputs.config_spec("llama2_7b")) == 1
     assert routed(inputs.config_spec("llama2_7b_fp8")) == 1
     assert routed(inputs.config_spec("llama2_7b"), sched_mode=B.SCHED_SPLIT) == 0
-    for name in ("tiny", "llama3_8b", "l70b_tp1", "batched"):       # GQA, or one-unit
+    for name in ("tiny", "llama3_8b", "l70b_tp1"):       # GQA with one request, or one-unit
         assert routed(inputs.config_spec(name)) == 0, name
     big = inputs.custom_spec("mha_big_prefill", 32, 32, [(4096, 12288)], [8192] * 128, seed=1)
     assert routed(big) == 0                                          # share ~0.24
@@ -448,3 +448,26 @@ def test_one_unit_roles_follow_prefill_request_count():
         assert f.info()["one_unit_per_wg"] == 0
     i = _spec_lists(inputs.config_spec("llama3_8b")).info()
     assert i["one_unit_per_wg"] == 1 and i["sched_mode"] == B.SCHED_COLOCATE
+
+
+def test_gqa_small_prefill_share_runs_on_two_streams():
+    """Automatic scheduling runs a GQA batch with several prefill requests,
+    too many units for the one-unit launch and a prefill under 0.15 of the
+    estimated work on two streams (runs_sequential 2); one prefill request,
+    a larger share, MHA or an explicit mode keep their launch."""
+    def routed(spec, **tun):
+        p = B.make_params(spec.num_qo_heads, spec.num_kv_heads, spec.layout, spec.page_size,
+                          spec.causal, spec.sm_scale, kv_dtype=spec.kv_dtype)
+        t = B.make_tuning(**tun) if tun else None
+        return B.plan_host(p, spec.prefill_qo_len, spec.prefill_kv_len, spec.decode_kv_len,
+                           t).info()["runs_sequential"]
+    assert routed(inputs.config_spec("batched")) == 2                    # share 0.09
+    assert routed(inputs.config_spec("batched", n_dec=256)) == 2         # 0.11
+    assert routed(inputs.config_spec("batched", n_dec=128)) == 0         # 0.17
+    assert routed(inputs.config_spec("batched_fp8")) == 0                # 0.16
+    assert routed(inputs.config_spec("batched", n_dec=64)) == 0          # one-unit launch
+    assert routed(inputs.config_spec("batched"), sched_mode=B.SCHED_SPLIT) == 0
+    rng = np.random.default_rng(13)
+    one = inputs.custom_spec("one_chunk", 32, 8, [(512, 8192)],
+                             list(rng.integers(512, 16384, 256)), seed=13)
+    assert routed(one) == 0                                              # one request
