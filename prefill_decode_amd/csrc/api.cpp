@@ -652,18 +652,15 @@ namespace {
 // Prefill kernel on `stream`, decode kernel on `decode_stream` (forked from
 // and joined back to `stream` by events), then the merge on `stream`;
 // `before` / `after` (may be NULL) are recorded on `stream` around the two
-// kernels.
+// kernels.  Only the prefill kernel claims work through the counters (the
+// decode kernel runs one group per workgroup of its grid), so the two
+// kernels running at once share the sequential kind's counter block safely,
+// captured (self-resetting) or not.
 pod_status_t run_streams(pod_attn_plan_t pl, const pod_attn_tensors_t* t, hipStream_t stream,
                          hipStream_t decode_stream, hipEvent_t before, hipEvent_t after) {
   const WorkLists& w = pl->seq_is_fused ? pl->fused : pl->seq;
   KernelArgs a = make_args(pl, t, w, pl->dl_seq);
   pick_counters(pl, kKindSeq, stream, &a);
-  // the decode kernel claims from a counter block of its own (the fused
-  // kind's, which a plan run this way does not launch): the two kernels run
-  // at once, and a captured (self-resetting) launch resets its whole block
-  // when its last workgroup ends
-  KernelArgs ad = a;
-  pick_counters(pl, kKindFused, stream, &ad);
   hipError_t e;
   for (hipEvent_t* ev : {&pl->ev_fork, &pl->ev_join})
     if (!*ev && (e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess)
@@ -681,10 +678,9 @@ pod_status_t run_streams(pod_attn_plan_t pl, const pod_attn_tensors_t* t, hipStr
     if (!a.self_reset) ++pl->launches[kKindSeq];
   }
   if (w.n_groups() > 0 &&
-      (e = is_fp8(pl) ? launch_decode_fp8(ad, kvm, w.n_groups(), decode_stream)
-                      : launch_decode(ad, kvm, w.n_groups(), decode_stream)) != hipSuccess)
+      (e = is_fp8(pl) ? launch_decode_fp8(a, kvm, w.n_groups(), decode_stream)
+                      : launch_decode(a, kvm, w.n_groups(), decode_stream)) != hipSuccess)
     return hip_err(e, "decode kernel launch");
-  if (w.n_groups() > 0 && !ad.self_reset) ++pl->launches[kKindFused];
   // join: the merge (and whatever the caller enqueues next) waits for both
   if ((e = hipEventRecord(pl->ev_join, decode_stream)) != hipSuccess)
     return hip_err(e, "hipEventRecord");

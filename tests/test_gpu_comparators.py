@@ -163,3 +163,24 @@ def test_gqa_small_prefill_runs_on_two_streams():
     assert f.plan.info()["runs_sequential"] == 0
     del r, f, bd
     torch.cuda.empty_cache()
+
+
+def test_paths_interleaved_keep_their_counters():
+    """Runs of every path of one plan, interleaved (fused, two streams, fused,
+    sequential, batched prefill, fused): each fused run finds its counter
+    block zeroed whatever ran before it, so every fused output is the same
+    and matches the oracle (a counter block left dirty by another path would
+    make the fused kernel skip its work)."""
+    spec = reduced_specs()[1]
+    say(f"[interleaved paths] {spec.name}")
+    b = inputs.make_batch_host(spec, poison=True)
+    ref = oracle.batch_attention(b)
+    r = B.BatchRunner(b, B.make_tuning(flags=B.FLAG_BATCHED_PREFILL, sched_mode=B.SCHED_SPLIT))
+    first = run_path(r, "fused")
+    compare(first, ref, f"{spec.name}/fused")
+    for path in ("streams", "fused", "seq", "batched", "fused", "fused"):
+        got = run_path(r, path)
+        compare(got, ref, f"{spec.name}/{path}")
+        if path == "fused":
+            for k in first:
+                assert np.array_equal(got[k], first[k]), (path, k)
