@@ -161,7 +161,9 @@ constexpr double kMhaSequentialShare = 0.2;
 // two streams led with 128 decodes (0.17: 838 / 795 / 835) and on the FP8
 // mix (0.16: 715 / 696 / 771), the fused launch on a 64-head layer with two
 // 256-token chunks and 256 decodes (0.16: 1,307 / 1,334 / 1,332); the bound
-// sits below all three.
+// sits below all three.  On five more shapes below it (32 or 64 query heads
+// over 8 KV heads, 2-4 chunks, 160-384 decodes, shares 0.09-0.15) the two
+// routes were within 1.5% of each other, either way.
 constexpr double kGqaStreamsShare = 0.15;
 
 // Automatic launch shape: batches of at most kOneUnitSlotsFactor fused units
