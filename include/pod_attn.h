@@ -322,7 +322,8 @@ pod_status_t pod_attn_plan_shared_prefix_host(const pod_attn_params_t* params,
  * (runs use it with pod_attn_run / pod_attn_sequential_run / ... as usual).
  * Allocates no device memory (no hipMalloc, hipFree or allocating library
  * routine; the plan object itself is host memory, freed by
- * pod_attn_plan_destroy).  The scratch is shared by every such plan on the
+ * pod_attn_plan_destroy) and creates no stream: a batch that pod_attn_plan
+ * would run on two streams runs as one fused launch here.  The scratch is shared by every such plan on the
  * device: a new pod_attn_plan_scratch call overwrites the work lists and
  * counters of the previous one, so only the most recent scratch plan of a
  * device may run, and runs that overlap in time race.  The counters are

@@ -507,12 +507,16 @@ pod_status_t pod_attn_plan_host(const pod_attn_params_t* params, int32_t num_pre
   return POD_OK;
 }
 
-pod_status_t pod_attn_plan(const pod_attn_params_t* params, int32_t num_prefill,
-                           const int32_t* prefill_qo_len, const int32_t* prefill_kv_len,
-                           int32_t num_decode, const int32_t* decode_kv_len,
-                           const pod_attn_tuning_t* tuning, void* workspace,
-                           size_t workspace_bytes, size_t* workspace_needed, hipStream_t stream,
-                           pod_attn_plan_t* out_plan) {
+namespace {
+
+// pod_attn_plan; with `no_streams` a batch the planner would run on two
+// streams runs the fused launch instead (no stream is created).
+pod_status_t plan_on_device(const pod_attn_params_t* params, int32_t num_prefill,
+                            const int32_t* prefill_qo_len, const int32_t* prefill_kv_len,
+                            int32_t num_decode, const int32_t* decode_kv_len,
+                            const pod_attn_tuning_t* tuning, void* workspace,
+                            size_t workspace_bytes, size_t* workspace_needed, hipStream_t stream,
+                            pod_attn_plan_t* out_plan, bool no_streams) {
   if (out_plan) *out_plan = nullptr;
   if (!workspace_needed && !workspace)
     return set_err(POD_ERR_INVALID_ARGUMENT, "workspace and workspace_needed are both NULL");
@@ -532,8 +536,22 @@ pod_status_t pod_attn_plan(const pod_attn_params_t* params, int32_t num_prefill,
     delete pl;
     return st;
   }
+  if (no_streams && pl->choice.runs_sequential == 2) pl->choice.runs_sequential = 0;
   return finish_device_plan(pl, device, workspace, workspace_bytes, workspace_needed, stream,
                             out_plan);
+}
+
+}  // namespace
+
+pod_status_t pod_attn_plan(const pod_attn_params_t* params, int32_t num_prefill,
+                           const int32_t* prefill_qo_len, const int32_t* prefill_kv_len,
+                           int32_t num_decode, const int32_t* decode_kv_len,
+                           const pod_attn_tuning_t* tuning, void* workspace,
+                           size_t workspace_bytes, size_t* workspace_needed, hipStream_t stream,
+                           pod_attn_plan_t* out_plan) {
+  return plan_on_device(params, num_prefill, prefill_qo_len, prefill_kv_len, num_decode,
+                        decode_kv_len, tuning, workspace, workspace_bytes, workspace_needed,
+                        stream, out_plan, false);
 }
 
 pod_status_t pod_attn_plan_shared_prefix(const pod_attn_params_t* params, int32_t num_decode,
@@ -598,8 +616,11 @@ pod_status_t pod_attn_plan_scratch(const pod_attn_params_t* params, int32_t num_
   if ((e = scratch_address(device, &ws)) != hipSuccess)
     return hip_err(e, "hipGetSymbolAddress(scratch)");
   size_t need = 0;
-  pod_status_t st = pod_attn_plan(params, num_prefill, prefill_qo_len, prefill_kv_len, num_decode,
-                                  decode_kv_len, tuning, nullptr, 0, &need, stream, nullptr);
+  // the two-stream route creates a stream: plans made here run those
+  // batches as one fused launch instead
+  pod_status_t st = plan_on_device(params, num_prefill, prefill_qo_len, prefill_kv_len,
+                                   num_decode, decode_kv_len, tuning, nullptr, 0, &need, stream,
+                                   nullptr, true);
   if (st != POD_OK) return st;
   if (need > kScratchBytes) {
     char buf[200];
@@ -608,8 +629,8 @@ pod_status_t pod_attn_plan_scratch(const pod_attn_params_t* params, int32_t num_
                   "pod_attn_plan with a caller workspace)", need, kScratchBytes);
     return set_err(POD_ERR_WORKSPACE_TOO_SMALL, buf);
   }
-  return pod_attn_plan(params, num_prefill, prefill_qo_len, prefill_kv_len, num_decode,
-                       decode_kv_len, tuning, ws, kScratchBytes, &need, stream, out_plan);
+  return plan_on_device(params, num_prefill, prefill_qo_len, prefill_kv_len, num_decode,
+                        decode_kv_len, tuning, ws, kScratchBytes, &need, stream, out_plan, true);
 }
 
 namespace {

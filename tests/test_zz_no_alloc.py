@@ -65,3 +65,33 @@ def test_scratch_plan_too_large_is_refused():
     with pytest.raises(B.PodError) as e:
         B.plan_scratch(p, spec.prefill_qo_len, spec.prefill_kv_len, spec.decode_kv_len)
     assert e.value.status == 3 and "static scratch" in str(e.value)
+
+
+def test_scratch_plan_keeps_the_fused_launch_for_two_stream_batches():
+    """A batch pod_attn_plan runs on two streams (the batched mix) runs the
+    fused launch from a scratch plan (which creates no stream), with the same
+    results as the workspace plan's two-stream run within the parity bar."""
+    import torch
+    spec = inputs.config_spec("batched")
+    say("[scratch] batched: generating on device")
+    bd = inputs.make_batch_device(spec, poison=True)
+    runner = B.BatchRunner(bd)
+    assert runner.plan.info()["runs_sequential"] == 2
+    plan = B.plan_scratch(runner.params, spec.prefill_qo_len, spec.prefill_kv_len,
+                          spec.decode_kv_len)
+    assert plan.info()["runs_sequential"] == 0
+    want = run_path(runner, "fused")
+    got = _run_plan(runner, plan, "fused")
+    rows = [0, 127, 128, 383, 384, 895, 896, 1535]
+    dec = [0, 1, 95, 191]
+    sub = inputs.host_subset(bd, list(range(spec.num_prefill)), dec)
+    ref = oracle.sample_batch_attention(sub, rows, list(range(len(dec))))
+    for g in (want, got):
+        compare({"o_prefill": g["o_prefill"][rows], "lse_prefill": g["lse_prefill"][rows],
+                 "o_decode": g["o_decode"][dec], "lse_decode": g["lse_decode"][dec]},
+                ref, "batched/scratch")
+        for k in g:
+            assert np.all(np.isfinite(g[k])), k
+    plan.destroy()
+    del runner, bd
+    torch.cuda.empty_cache()
